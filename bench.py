@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one forward pass (fa_fwd through the C ABI) over the whole
+workload with inputs already resident in HBM.  Default workload: causal GQA,
+batch 2, 32 query heads, 8 key/value heads, seqlen 8192, head_dim 128, bf16.
+Prints ONE JSON line with the throughput in causal-adjusted TFLOPS
+(FLOPs = 2 * (D + Dv) * Hq * admissible (query, key) pairs; softmax not
+counted), the roofline of the kernel against the MI355X dense MFMA peak, and
+the fp64 CPU oracle timed on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS (causal-adjusted) and % of bf16 MFMA peak, 1 MI355X"
+DEFAULT_WORKLOAD = "gqa_causal_b2_hq32_hkv8_s8192_d128"
+# MI355X published dense peaks (TFLOP/s): bf16 2.5 PFLOP/s, fp8 5.0 PFLOP/s.
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def pairs_per_sequence(sq: int, sk: int, causal: bool) -> int:
+    """Admissible (query, key) pairs of one sequence.  Under bottom-right causal alignment row i
+    sees min(max(i + sk - sq + 1, 0), sk) keys; the sum over rows is taken in closed form."""
+    if not causal:
+        return sq * sk
+
+    def s(n: int) -> int:  # sum_{x=1..n} min(x, sk), n >= 0
+        if n <= sk:
+            return n * (n + 1) // 2
+        return sk * (sk + 1) // 2 + (n - sk) * sk
+
+    a = sk - sq + 1  # keys seen by row 0 (before clipping)
+    b = a + sq - 1  # keys seen by row sq-1 (before clipping)
+    return s(max(b, 0)) - s(max(a - 1, 0))
+
+
+def workload_flops(w) -> int:
+    pairs = sum(pairs_per_sequence(sq, sk, w.causal) for sq, sk in w.lengths)
+    return 2 * (w.head_dim + w.head_dim_v) * w.heads_q * pairs
+
+
+def row_flops(w, b: int, i: int) -> int:
+    sq, sk = w.lengths[b]
+    n = min(sk, i + sk - sq + 1) if w.causal else sk
+    return 2 * (w.head_dim + w.head_dim_v) * max(n, 0)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_forward_fa_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch from the committed rocprofv3 PMC summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float):
+    """The fp64 oracle on a random row sample of the workload; TFLOPS in the metric's unit."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(1234)
+    rows, flops = [], 0
+
+    def draw(n):
+        nonlocal flops
+        out = []
+        for _ in range(n):
+            b = int(rng.integers(0, w.batch))
+            sq = w.lengths[b][0]
+            if sq == 0:
+                continue
+            i = int(rng.integers(0, sq))
+            h = int(rng.integers(0, w.heads_q))
+            out.append((b, h, i))
+            flops += row_flops(w, b, i)
+        return out
+
+    dt = oracle.BF16 if w.dtype == "bf16" else oracle.E4M3
+    kw = w.shape_kwargs()
+    # calibrate on a small sample, then size the measured sample to about target_s seconds
+    cal = draw(max(16, oracle.num_threads()))
+    t0 = time.perf_counter()
+    oracle.attention_rows(w.q, w.k, w.v, cal, descales=w.descales, dtype=dt, **kw)
+    t_cal = time.perf_counter() - t0
+    rate = flops / max(t_cal, 1e-6)
+    flops = 0
+    n = 16
+    rows = draw(n)
+    while flops < rate * target_s and len(rows) < 1_000_000:
+        rows += draw(len(rows))
+    t0 = time.perf_counter()
+    oracle.attention_rows(w.q, w.k, w.v, rows, descales=w.descales, dtype=dt, **kw)
+    sec = time.perf_counter() - t0
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOPS", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} random (batch, head, query) rows of the same workload, "
+                      f"{flops:.3e} causal-adjusted FLOPs in {sec:.1f} s (fp64)"}
+
+
+def copy_calibration(nbytes: int) -> None:
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters of the attention kernel."""
+    import torch
+
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"copied {nbytes} bytes x3")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a device copy of BYTES bytes (counter scaling) and exit")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported by this "
+              "single-GPU build (the kernel's multi-GPU sharding is a design note, not code).",
+              file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
+
+    import torch
+
+    import fa_inputs
+    import exact_attention_forward_fa_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    w = fa_inputs.workload(args.workload)
+    log(f"workload {w.name}: batch={w.batch} hq={w.heads_q} hkv={w.heads_kv} sq={w.seqlen_q} "
+        f"sk={w.seqlen_k} d={w.head_dim} causal={w.causal} dtype={w.dtype}")
+    q, k, v = w.q.cuda(), w.k.cuda(), w.v.cuda()
+    cu = torch.from_numpy(w.cu_seqlens).cuda() if w.cu_seqlens is not None else None
+    ds = torch.from_numpy(w.descales).cuda() if w.descales is not None else None
+    o = torch.empty((w.total_q, w.heads_q, w.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fa_fwd(q, k, v, o, lse, w.batch, w.heads_q, w.heads_kv, w.seqlen_q, w.seqlen_k, cu,
+                  w.head_dim, w.head_dim_v, w.softmax_scale, int(w.causal), ds,
+                  stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    flops = workload_flops(w)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"kernel {kernel_ms:.4f} ms/launch (events), wall {ms_per_step:.4f} ms/step, "
+        f"{achieved:.1f} TFLOPS = {100 * achieved / peak:.1f}% of {peak:.0f}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a row sample ...")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"oracle: {cpu}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100 * value / peak, 2),
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q,
+                   "heads_kv": w.heads_kv, "seqlen_q": w.seqlen_q, "seqlen_k": w.seqlen_k,
+                   "head_dim": w.head_dim, "head_dim_v": w.head_dim_v, "causal": w.causal,
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": load_traffic(w.name), "kernel_ms": round(kernel_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

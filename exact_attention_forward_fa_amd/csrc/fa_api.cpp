@@ -1,0 +1,153 @@
+// fa_api.cpp -- the C ABI of libfa_fwd.so: argument validation, the
+// shared-memory (LDS) screen, the planner and the launch call.
+//
+// Everything here except the final fa::launch is plain host arithmetic with
+// no HIP call, so every error a caller can make with sizes or pointers is
+// reported before the device is touched.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa_fwd.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// gfx950 (MI355X): 160 KiB LDS per CU, all of it addressable by one
+// workgroup; 256 CUs; 4 SIMDs per CU; 512 VGPR+AGPR per lane per SIMD;
+// 8 wave slots per SIMD.
+constexpr fa_device_limits_t kGfx950 = {163840, 163840, 256, 4, 512, 8};
+
+int check_dims(int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k, int head_dim,
+               int head_dim_v) {
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || seqlen_q < 0 || seqlen_k < 0 ||
+      head_dim <= 0 || head_dim_v <= 0)
+    return FA_ERR_INVALID;
+  if (heads_q % heads_kv != 0) return FA_ERR_INVALID;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 100; }
+
+const char* fa_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_INVALID: return "invalid argument (sizes, head ratio or softmax scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dims or no tile plan fits)";
+    case FA_ERR_DEVICE: return "device error (not gfx950, or the kernel launch failed)";
+    default: return "unknown error code";
+  }
+}
+
+int fa_gfx950_limits(fa_device_limits_t* out) {
+  if (!out) return FA_ERR_NULL;
+  *out = kGfx950;
+  return FA_OK;
+}
+
+// Byte accounting of the shared-memory screen: with Q staged in shared
+// memory the Q, K and V tiles add up (K and V once per stage); with Q kept
+// in registers after the prologue, the Q buffer and the V buffers have
+// disjoint lifetimes and share space, so they combine by max.
+int fa_smem_screen(const fa_tile_config_t* cfg, const fa_device_limits_t* dev, fa_screen_t* out) {
+  if (!cfg || !dev || !out) return FA_ERR_NULL;
+  if (cfg->tile_m <= 0 || cfg->tile_n <= 0 || cfg->head_dim <= 0 || cfg->head_dim_v <= 0 ||
+      cfg->elem_bytes <= 0 || cfg->kv_stages <= 0 || dev->lds_bytes_per_block <= 0 ||
+      dev->lds_bytes_per_cu <= 0)
+    return FA_ERR_INVALID;
+  const int64_t e = cfg->elem_bytes;
+  const int64_t q = (int64_t)cfg->tile_m * cfg->head_dim * e;
+  const int64_t k = (int64_t)cfg->tile_n * cfg->head_dim * e * cfg->kv_stages;
+  const int64_t v = (int64_t)cfg->tile_n * cfg->head_dim_v * e * cfg->kv_stages;
+  out->smem_bytes = cfg->q_in_regs ? k + (q > v ? q : v) : q + k + v;
+  out->fits = out->smem_bytes <= dev->lds_bytes_per_block;
+  out->blocks_per_cu = out->fits ? (int)(dev->lds_bytes_per_cu / out->smem_bytes) : 0;
+  return FA_OK;
+}
+
+int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
+                int varlen, int head_dim, int head_dim_v, int causal,
+                const fa_device_limits_t* dev, fa_plan_t* out) {
+  (void)varlen;
+  (void)causal;
+  if (!out) return FA_ERR_NULL;
+  int rc = check_dims(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, head_dim_v);
+  if (rc) return rc;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_E4M3) return FA_ERR_INVALID;
+  if ((head_dim != 64 && head_dim != 128) || head_dim_v != head_dim) return FA_ERR_UNSUPPORTED;
+  const fa_device_limits_t& L = dev ? *dev : kGfx950;
+  if (L.lds_bytes_per_block <= 0 || L.lds_bytes_per_cu <= 0 || L.simds_per_cu <= 0 ||
+      L.regs_per_simd_lane <= 0)
+    return FA_ERR_INVALID;
+  // The compiled kernel: 128 query rows (4 waves x 32), 64-key blocks, K/V
+  // double-buffered in LDS with padded rows, Q in registers, 256 VGPR+AGPR
+  // per lane (2 waves per SIMD).
+  const int64_t lds = fa::lds_bytes(head_dim);
+  if (lds > L.lds_bytes_per_block) return FA_ERR_UNSUPPORTED;
+  const int vgprs = 256;
+  const int by_lds = (int)(L.lds_bytes_per_cu / lds);
+  const int waves_per_simd_by_regs = L.regs_per_simd_lane / vgprs;
+  const int by_regs = waves_per_simd_by_regs * L.simds_per_cu / fa::kWaves;
+  out->tile_m = fa::kTileM;
+  out->tile_n = fa::kTileN;
+  out->waves = fa::kWaves;
+  out->kv_stages = fa::kStages;
+  out->lds_bytes = lds;
+  out->wg_per_cu = by_lds < by_regs ? by_lds : by_regs;
+  out->vgprs_per_lane = vgprs;
+  out->m_tiles = (seqlen_q + fa::kTileM - 1) / fa::kTileM;
+  out->num_workgroups = (int64_t)out->m_tiles * heads_q * batch;
+  out->kernel_variant = (head_dim == 128 ? 0 : 2) + (causal ? 1 : 0) + (dtype == FA_DTYPE_E4M3 ? 4 : 0);
+  if (out->wg_per_cu <= 0) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+           int heads_q, int heads_kv, int seqlen_q, int seqlen_k, const int* cu_seqlens,
+           int head_dim, int head_dim_v, float softmax_scale, int causal, const float* descales,
+           void* stream) {
+  int rc = check_dims(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, head_dim_v);
+  if (rc) return rc;
+  // Q/O/LSE may be NULL only when there is provably no query row, K/V only
+  // when there is provably no key (fixed-length calls with a zero length).
+  if ((!q || !o || !lse) && (cu_seqlens || seqlen_q > 0)) return FA_ERR_NULL;
+  if ((!k || !v) && (cu_seqlens || seqlen_k > 0)) return FA_ERR_NULL;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  const int dtype = descales ? FA_DTYPE_E4M3 : FA_DTYPE_BF16;
+  fa_plan_t plan;
+  rc = fa_fwd_plan(dtype, batch, heads_q, heads_kv, seqlen_q, seqlen_k, cu_seqlens != nullptr,
+                   head_dim, head_dim_v, causal, nullptr, &plan);
+  if (rc) return rc;
+  if (plan.num_workgroups > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (plan.num_workgroups == 0) return FA_OK;  // no query rows: nothing to write
+  fa::Launch L;
+  L.p.q = q;
+  L.p.k = k;
+  L.p.v = v;
+  L.p.o = o;
+  L.p.lse = lse;
+  L.p.cu = cu_seqlens;
+  L.p.descales = descales;
+  L.p.batch = batch;
+  L.p.hq = heads_q;
+  L.p.hkv = heads_kv;
+  L.p.group = heads_q / heads_kv;
+  L.p.seqlen_q = seqlen_q;
+  L.p.seqlen_k = seqlen_k;
+  L.p.m_tiles = plan.m_tiles;
+  L.p.scale_log2 = softmax_scale * kLog2e;
+  L.head_dim = head_dim;
+  L.causal = causal;
+  L.fp8 = dtype == FA_DTYPE_E4M3;
+  L.num_workgroups = plan.num_workgroups;
+  return fa::launch(L, stream);
+}
+
+}  // extern "C"

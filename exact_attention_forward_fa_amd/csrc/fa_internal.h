@@ -1,0 +1,49 @@
+// fa_internal.h -- what the C-ABI layer (fa_api.cpp) hands to the kernel
+// launcher (fa_fwd_kernel.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+// Kernel geometry shared by the planner and the launcher.
+constexpr int kTileM = 128;  // query rows per workgroup (4 waves x 32 rows)
+constexpr int kTileN = 64;   // keys per main-loop step
+constexpr int kWaves = 4;    // wavefronts per workgroup
+constexpr int kStages = 2;   // K/V LDS buffers
+
+// LDS row pitch (bytes) of the K and V tiles.  K rows are read 16 B per lane
+// by 16 consecutive rows per LDS cycle, so the pitch is an odd multiple of
+// 16 B; V rows are read by the transposing 8 B loads four rows at a time, so
+// the pitch is 64 B mod 256 B and four consecutive rows cover all 64 banks.
+constexpr int k_lds_pitch(int d) { return d * 2 + 16; }
+constexpr int v_lds_pitch(int d) { return d * 2 + 64; }
+constexpr int64_t lds_bytes(int d) {
+  return (int64_t)kStages * kTileN * (k_lds_pitch(d) + v_lds_pitch(d));
+}
+
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int* cu;          // NULL or int32[2*(batch+1)]
+  const float* descales;  // NULL or float[3]
+  int batch, hq, hkv, group, seqlen_q, seqlen_k;
+  int m_tiles;            // query tiles per (sequence, head)
+  float scale_log2;       // softmax_scale * log2(e)
+};
+
+struct Launch {
+  Params p;
+  int head_dim;
+  int causal;
+  int fp8;
+  int64_t num_workgroups;
+};
+
+// Returns 0, or FA_ERR_DEVICE when the device is not gfx950 or the launch fails.
+int launch(const Launch& L, void* stream);
+
+}  // namespace fa

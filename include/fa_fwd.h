@@ -1,0 +1,171 @@
+/*
+ * fa_fwd.h -- C ABI of the MI355X (gfx950) exact-attention forward library
+ * (libfa_fwd.so).
+ *
+ * The operation is the FlashAttention forward pass dissected by the pages
+ * "FlashAttention core algorithm: forward pass" (the Hopper kernel's
+ * consumer loop: per query tile S = Q K^T, online softmax with the scale
+ * folded into softmax_scale_log2, O += P V, then the epilogue's store or
+ * store_zero) and "Dissecting the SM_120 Microarchitecture" (section 11.2,
+ * FlashAttention bottleneck analysis, Fig. 12).  For every sequence b,
+ * query head h and query row i:
+ *
+ *   g    = h / (heads_q / heads_kv)                      grouped-query heads
+ *   A_i  = { j < sk_b : not causal or j <= i + sk_b - sq_b }   bottom-right
+ *   s_ij = softmax_scale * q_i . k_j                    (q_descale*k_descale
+ *                                                        folded in for fp8)
+ *   O_i  = sum_{j in A_i} softmax_j(s_i) v_j             (times v_descale)
+ *   LSE_i = ln sum_{j in A_i} exp(s_ij)
+ *   A_i empty: O_i = 0, LSE_i = -inf    (the epilogue's store_zero rule)
+ *
+ * Data types: without descales Q, K, V are bf16; with descales they are OCP
+ * fp8 e4m3 ("e4m3fn") codes.  O is always bf16 (round to nearest even), LSE
+ * always fp32.
+ *
+ * Layouts (contiguous, no strides):
+ *   Q [total_q][heads_q][head_dim]     K [total_k][heads_kv][head_dim]
+ *   V [total_k][heads_kv][head_dim_v]  O [total_q][heads_q][head_dim_v]
+ *   LSE [heads_q][total_q]
+ *   cu_seqlens == NULL: total_q = batch*seqlen_q, total_k = batch*seqlen_k.
+ *   cu_seqlens != NULL: int32[2*(batch+1)]; cu_seqlens[0..batch] are the
+ *     query offsets, cu_seqlens[batch+1 .. 2*batch+1] the key offsets of a
+ *     packed batch; seqlen_q / seqlen_k are then the largest sequence
+ *     lengths (they size the launch grid).  Offsets must be non-decreasing,
+ *     start at 0 and every length must be <= the maximum passed: this is the
+ *     caller's contract and is not checked on the device.
+ *
+ * Ownership: every pointer belongs to the caller; the library allocates no
+ * device memory and keeps no per-call state (it caches one device-property
+ * query per device).  Calls are asynchronous on `stream`; a device fault
+ * surfaces at the caller's next synchronisation.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes.  Codes FA_ERR_NULL .. FA_ERR_UNSUPPORTED are decided on the
+ * host before any HIP call. */
+#define FA_OK 0
+#define FA_ERR_NULL (-1)        /* a required pointer is NULL                       */
+#define FA_ERR_INVALID (-2)     /* bad sizes, heads_q % heads_kv != 0, bad scale     */
+#define FA_ERR_UNSUPPORTED (-3) /* head_dim not in {64,128}, head_dim_v != head_dim,
+                                   or no tile plan fits the device                   */
+#define FA_ERR_DEVICE (-4)      /* not a gfx950 device, or the launch failed         */
+
+/* Input type selector for the planner (fa_fwd itself infers it from
+ * `descales`). */
+#define FA_DTYPE_BF16 0
+#define FA_DTYPE_E4M3 1
+
+/*
+ * fa_fwd -- launch the forward pass on `stream` (a hipStream_t; NULL is the
+ * null stream).
+ *
+ *   q, k, v     device pointers, layouts above (bf16, or e4m3 codes when
+ *               descales != NULL)
+ *   o           device pointer, bf16 [total_q][heads_q][head_dim_v] (output)
+ *   lse         device pointer, fp32 [heads_q][total_q] (output)
+ *   batch, heads_q, heads_kv   > 0, heads_q % heads_kv == 0
+ *   seqlen_q, seqlen_k         >= 0 (maxima when cu_seqlens != NULL)
+ *   cu_seqlens  NULL or device int32[2*(batch+1)] (see above)
+ *   head_dim, head_dim_v       64 or 128, equal
+ *   softmax_scale              finite and > 0 (usually 1/sqrt(head_dim))
+ *   causal      0: every key of the sequence; 1: bottom-right causal mask
+ *   descales    NULL (bf16 inputs) or device float[3] = {q, k, v} descale
+ *               factors of e4m3 inputs: q*k descale multiplies the scores,
+ *               v descale the output
+ *
+ * q, o and lse may be NULL only for a fixed-length call with seqlen_q == 0;
+ * k and v only for a fixed-length call with seqlen_k == 0.
+ *
+ * Returns FA_OK or a negative code (fa_strerror).  Rows of a sequence with
+ * no admissible key get O = 0 and LSE = -inf; nothing is written for
+ * sequences with no query.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+           int heads_q, int heads_kv, int seqlen_q, int seqlen_k, const int* cu_seqlens,
+           int head_dim, int head_dim_v, float softmax_scale, int causal, const float* descales,
+           void* stream);
+
+/* Text for a return code (static storage, never NULL). */
+const char* fa_strerror(int code);
+
+/* ---- tile / occupancy screening (pure host functions) ------------------ */
+
+/*
+ * Capacity figures of a device, as the shared-memory screen of "FlashAttention
+ * on SM120 reusing the SM80 forward" (section on can_implement and the
+ * appendix table of per-SM / per-block shared memory) uses them.  On gfx950
+ * the "shared memory" is the LDS: 160 KiB per compute unit, all of it
+ * available to one workgroup.
+ */
+typedef struct fa_device_limits {
+  int64_t lds_bytes_per_block; /* largest allocation one workgroup may hold  */
+  int64_t lds_bytes_per_cu;    /* total shared by resident workgroups        */
+  int num_cus;                 /* compute units (SMs)                         */
+  int simds_per_cu;            /* 4 on gfx950                                 */
+  int regs_per_simd_lane;      /* VGPR+AGPR per lane per SIMD (512 on gfx950) */
+  int max_waves_per_simd;      /* hardware wave slots per SIMD                */
+} fa_device_limits_t;
+
+/* One candidate tile configuration, in the page's terms. */
+typedef struct fa_tile_config {
+  int tile_m;      /* query rows per block                                */
+  int tile_n;      /* keys per main-loop step                             */
+  int head_dim;    /* D                                                   */
+  int head_dim_v;  /* Dv                                                  */
+  int elem_bytes;  /* bytes per Q/K/V element (2 bf16, 1 fp8)             */
+  int kv_stages;   /* K/V buffers (1 single-stage, 2 double-stage)        */
+  int q_in_regs;   /* 1: Q lives in registers after the prologue, so its
+                      buffer shares space with V (max instead of sum)     */
+} fa_tile_config_t;
+
+typedef struct fa_screen {
+  int64_t smem_bytes; /* Q + stages*(K + V), or K*stages + max(Q, V*stages) */
+  int fits;           /* smem_bytes <= lds_bytes_per_block                  */
+  int blocks_per_cu;  /* floor(lds_bytes_per_cu / smem_bytes) when it fits  */
+} fa_screen_t;
+
+/* The page's byte accounting and fit verdict for one configuration.
+ * Returns FA_OK, FA_ERR_NULL or FA_ERR_INVALID (non-positive sizes). */
+int fa_smem_screen(const fa_tile_config_t* cfg, const fa_device_limits_t* dev, fa_screen_t* out);
+
+/* The gfx950 (MI355X) figures used when a planner call passes dev == NULL. */
+int fa_gfx950_limits(fa_device_limits_t* out);
+
+/* The plan fa_fwd would launch for a shape. */
+typedef struct fa_plan {
+  int tile_m;            /* query rows per workgroup                          */
+  int tile_n;            /* keys per main-loop iteration                      */
+  int waves;             /* wavefronts per workgroup                          */
+  int kv_stages;         /* LDS buffers for K/V                               */
+  int64_t lds_bytes;     /* LDS per workgroup, as the kernel lays it out      */
+  int wg_per_cu;         /* resident workgroups per CU (LDS and VGPR limits)  */
+  int vgprs_per_lane;    /* VGPR+AGPR budget per lane the kernel is built for */
+  int64_t num_workgroups;/* grid size                                         */
+  int m_tiles;           /* query tiles per (sequence, head)                  */
+  int kernel_variant;    /* index of the compiled kernel                      */
+} fa_plan_t;
+
+/*
+ * fa_fwd_plan -- choose the kernel configuration for a shape (pure host
+ * function, no HIP call).  dev == NULL means gfx950.  Returns FA_OK,
+ * FA_ERR_NULL, FA_ERR_INVALID or FA_ERR_UNSUPPORTED (nothing fits `dev`).
+ */
+int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
+                int varlen, int head_dim, int head_dim_v, int causal,
+                const fa_device_limits_t* dev, fa_plan_t* out);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

@@ -1,0 +1,189 @@
+"""Host-side checks of libfa_fwd.so (no GPU): exported symbols, argument
+validation before any HIP call, the shared-memory screen against the page's
+worked figures, and the planner."""
+import ctypes
+import json
+import math
+import os
+import re
+
+import pytest
+
+import exact_attention_forward_fa_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KIB = 1024
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"fa_fwd", "fa_strerror", "fa_fwd_plan", "fa_smem_screen", "fa_gfx950_limits"} <= set(names)
+    lib = ctypes.CDLL(fa.library_path())
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_strerror_covers_codes():
+    for code in (0, -1, -2, -3, -4):
+        assert fa.fa_strerror(code) and "unknown" not in fa.fa_strerror(code)
+    assert "unknown" in fa.fa_strerror(-99)
+
+
+# Non-zero fake addresses: validation must reject these calls before touching them.
+P = 0x1000
+
+
+def call(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, batch=1, heads_q=4, heads_kv=2, seqlen_q=128,
+                seqlen_k=128, cu_seqlens=None, head_dim=128, head_dim_v=128, softmax_scale=0.1,
+                causal=0, descales=None, stream=0)
+    args.update(kw)
+    try:
+        return fa.fa_fwd(**args)
+    except fa.FaError as e:
+        return e.code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(k=None), fa.FA_ERR_NULL),
+    (dict(v=None), fa.FA_ERR_NULL),
+    (dict(o=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(batch=0), fa.FA_ERR_INVALID),
+    (dict(heads_q=0), fa.FA_ERR_INVALID),
+    (dict(heads_kv=0), fa.FA_ERR_INVALID),
+    (dict(heads_q=6, heads_kv=4), fa.FA_ERR_INVALID),
+    (dict(seqlen_q=-1), fa.FA_ERR_INVALID),
+    (dict(seqlen_k=-5), fa.FA_ERR_INVALID),
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID),
+    (dict(softmax_scale=-0.1), fa.FA_ERR_INVALID),
+    (dict(softmax_scale=math.inf), fa.FA_ERR_INVALID),
+    (dict(softmax_scale=math.nan), fa.FA_ERR_INVALID),
+    (dict(causal=2), fa.FA_ERR_INVALID),
+    (dict(head_dim=96, head_dim_v=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(head_dim=256, head_dim_v=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(head_dim=128, head_dim_v=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), fa.FA_ERR_INVALID),
+])
+def test_validation_before_any_hip_call(kw, code):
+    assert call(**kw) == code
+
+
+def test_empty_problem_is_a_no_op():
+    # no query rows: nothing to launch, so no device is needed either
+    assert call(q=None, o=None, lse=None, seqlen_q=0) == fa.FA_OK
+
+
+def _limits(name, fx):
+    d = fx["devices"][name]
+    L = fa.DeviceLimits()
+    L.lds_bytes_per_block = d["per_block_kib"] * KIB
+    L.lds_bytes_per_cu = d["per_sm_kib"] * KIB
+    L.num_cus, L.simds_per_cu, L.regs_per_simd_lane, L.max_waves_per_simd = 1, 4, 512, 8
+    return L
+
+
+@pytest.fixture(scope="module")
+def fixtures():
+    with open(os.path.join(ROOT, "tests", "golden", "smem_screen_page_fixtures.json")) as f:
+        return json.load(f)
+
+
+def test_screen_reproduces_page_tile_figures(fixtures):
+    for case in fixtures["tile_cases"]:
+        cfg = fa.TileConfig(**case["cfg"])
+        for dev, fits in case["fits"].items():
+            s = fa.fa_smem_screen(cfg, _limits(dev, fixtures))
+            assert s.smem_bytes == case["smem_kib"] * KIB
+            assert bool(s.fits) == fits, (case, dev)
+
+
+def _block_cfg(kib):
+    # a configuration whose buffers total exactly `kib` KiB: Q (kib-2) KiB + K 1 KiB + V 1 KiB
+    return fa.TileConfig(tile_m=kib - 2, tile_n=1, head_dim=1, head_dim_v=1, elem_bytes=KIB,
+                         kv_stages=1, q_in_regs=0)
+
+
+def test_screen_reproduces_page_block_examples(fixtures):
+    for case in fixtures["block_cases"]:
+        cfg = _block_cfg(case["block_kib"])
+        for dev, fits in case["fits"].items():
+            s = fa.fa_smem_screen(cfg, _limits(dev, fixtures))
+            assert s.smem_bytes == case["block_kib"] * KIB
+            assert bool(s.fits) == fits, (case, dev)
+        for dev, n in case.get("blocks_per_sm", {}).items():
+            assert fa.fa_smem_screen(cfg, _limits(dev, fixtures)).blocks_per_cu == n, (case, dev)
+
+
+def test_screen_q_in_regs_takes_max_of_q_and_v():
+    # Q and V buffers have disjoint lifetimes when Q lives in registers: K + max(Q, V)
+    cfg = fa.TileConfig(tile_m=128, tile_n=128, head_dim=128, head_dim_v=128, elem_bytes=2,
+                        kv_stages=1, q_in_regs=1)
+    s = fa.fa_smem_screen(cfg, fa.fa_gfx950_limits())
+    assert s.smem_bytes == 64 * KIB
+
+
+def test_screen_gfx950_answers():
+    g = fa.fa_gfx950_limits()
+    assert g.lds_bytes_per_block == 160 * KIB and g.lds_bytes_per_cu == 160 * KIB
+    one = fa.TileConfig(tile_m=128, tile_n=128, head_dim=128, head_dim_v=128, elem_bytes=2,
+                        kv_stages=1, q_in_regs=0)
+    two = fa.TileConfig(tile_m=128, tile_n=128, head_dim=128, head_dim_v=128, elem_bytes=2,
+                        kv_stages=2, q_in_regs=0)
+    s1, s2 = fa.fa_smem_screen(one, g), fa.fa_smem_screen(two, g)
+    assert (s1.fits, s1.blocks_per_cu) == (1, 1)   # 96 KiB
+    assert (s2.fits, s2.blocks_per_cu) == (1, 1)   # 160 KiB: exactly the gfx950 limit
+    assert fa.fa_smem_screen(_block_cfg(72), g).blocks_per_cu == 2
+    assert fa.fa_smem_screen(_block_cfg(161), g).fits == 0
+
+
+def test_screen_rejects_bad_sizes():
+    cfg = fa.TileConfig(tile_m=0, tile_n=64, head_dim=128, head_dim_v=128, elem_bytes=2,
+                        kv_stages=1, q_in_regs=0)
+    with pytest.raises(fa.FaError):
+        fa.fa_smem_screen(cfg, fa.fa_gfx950_limits())
+
+
+def test_plan_gfx950():
+    p = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 32, 8, 8192, 8192, False, 128, 128, True)
+    assert (p.tile_m, p.tile_n, p.waves, p.kv_stages) == (128, 64, 4, 2)
+    assert p.lds_bytes <= 80 * KIB and p.wg_per_cu == 2
+    assert p.m_tiles == 64 and p.num_workgroups == 64 * 32 * 2
+    p64 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 2, 2, 256, 256, False, 64, 64, False)
+    assert p64.m_tiles == 2 and p64.num_workgroups == 4 and p64.lds_bytes < p.lds_bytes
+
+
+def test_plan_reports_unsupported_when_nothing_fits():
+    small = fa.DeviceLimits(lds_bytes_per_block=64 * KIB, lds_bytes_per_cu=64 * KIB, num_cus=1,
+                            simds_per_cu=4, regs_per_simd_lane=512, max_waves_per_simd=8)
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 4, 4, 1024, 1024, False, 128, 128, True, small)
+    assert e.value.code == fa.FA_ERR_UNSUPPORTED
+
+
+def test_one_hip_runtime_when_package_is_imported_before_torch():
+    """Importing the package first must not leave two HIP runtimes in the process."""
+    import subprocess
+    import sys
+
+    code = ("import exact_attention_forward_fa_amd, torch\n"
+            "paths = set()\n"
+            "for line in open('/proc/self/maps'):\n"
+            "    if 'libamdhip64' in line:\n"
+            "        paths.add(os.path.realpath(line.split()[-1]))\n"
+            "print(len(paths), sorted(paths))\n")
+    r = subprocess.run([sys.executable, "-c", "import os\n" + code], capture_output=True, text=True,
+                       cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[0] == "1", r.stdout

@@ -1,0 +1,146 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  bf16: max|dO| <= 2e-2, max|dLSE| <= 1e-3; fp8 e4m3:
+5e-2 / 5e-3; rows with no admissible key exactly O = 0, LSE = -inf."""
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+from parity import compare, gather_rows, gpu_run, oracle_full, oracle_rows, sample_rows, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def full_check(w):
+    o, lse = gpu_run(w)
+    ro, rl = oracle_full(w)
+    return compare(o, lse, ro, rl, w.dtype, w.name)
+
+
+def sampled_check(w, n_random=24):
+    tensors = to_device(w)
+    o, lse = gpu_run(w, tensors)
+    rows = sample_rows(w, n_random=n_random, seed=w.seed)
+    say(f"[oracle] {len(rows)} sampled rows of {w.name}")
+    ro, rl = oracle_rows(w, rows)
+    og, lg = gather_rows(w, o, lse, rows)
+    compare(og, lg, ro, rl, w.dtype, w.name + " (sampled rows)")
+    return o, lse
+
+
+# ---------------------------------------------------------------- named workloads
+
+def test_tiny_noncausal_d64():
+    full_check(fa_inputs.workload("tiny_b1_h2_s256_d64"))
+
+
+@pytest.mark.parametrize("name", ["mha_b4_h16_s1024_d128", "mha_causal_b4_h16_s1024_d128"])
+def test_mha_1024(name):
+    full_check(fa_inputs.workload(name))
+
+
+def test_gqa_causal_8192_sampled():
+    w = fa_inputs.workload("gqa_causal_b2_hq32_hkv8_s8192_d128")
+    o, lse = sampled_check(w, n_random=32)
+    assert np.isfinite(lse).all() and np.isfinite(o).all()
+
+
+def test_varlen_causal_sampled():
+    w = fa_inputs.workload("varlen_causal_18seq_h16_d128")
+    o, lse = sampled_check(w, n_random=32)
+    # every row that sees no key (sk < sq, i < sq - sk) is exactly zero / -inf
+    cu = w.cu_seqlens
+    for b, (sq, sk) in enumerate(w.lengths):
+        dead = max(sq - sk, 0)
+        q0 = int(cu[b])
+        assert np.all(lse[:, q0:q0 + dead] == -np.inf)
+        assert np.all(o[q0:q0 + dead] == 0.0)
+        assert np.all(np.isfinite(lse[:, q0 + dead:q0 + sq]))
+
+
+def test_varlen_equals_per_sequence_calls():
+    """Packed varlen output equals separate fixed-length calls, bit for bit."""
+    lens = [(300, 517), (1, 64), (129, 100), (64, 0), (0, 40), (255, 256), (70, 700)]
+    w = fa_inputs.make(0, 4, 2, 0, 0, 128, causal=True, seed=50, lengths=lens, name="varlen_small")
+    o, lse = gpu_run(w)
+    ro, rl = oracle_full(w)
+    compare(o, lse, ro, rl, "bf16", w.name)
+    cu = w.cu_seqlens
+    nb = len(lens)
+    for b, (sq, sk) in enumerate(lens):
+        if sq == 0:
+            continue
+        q0, k0 = int(cu[b]), int(cu[nb + 1 + b])
+        wb = fa_inputs.make(1, 4, 2, sq, sk, 128, causal=True, seed=50, name=f"seq{b}")
+        wb.q, wb.k, wb.v = w.q[q0:q0 + sq], w.k[k0:k0 + sk], w.v[k0:k0 + sk]
+        if sk == 0:
+            wb.k = torch.zeros((0, 2, 128), dtype=torch.bfloat16)
+            wb.v = torch.zeros((0, 2, 128), dtype=torch.bfloat16)
+        ob, lb = gpu_run(wb)
+        assert np.array_equal(ob, o[q0:q0 + sq]), f"sequence {b}: O differs from packed call"
+        assert np.array_equal(lb, lse[:, q0:q0 + sq]), f"sequence {b}: LSE differs from packed call"
+
+
+# ----------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 4, 4, 300, 300), (1, 8, 2, 200, 517), (1, 4, 1, 517, 200),
+                                   (3, 2, 2, 1, 1), (1, 2, 2, 1, 333), (1, 32, 1, 130, 130)])
+def test_ragged_shapes(shape, causal, d):
+    b, hq, hkv, sq, sk = shape
+    w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq * 7 + sk + d,
+                       name=f"ragged_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}_c{int(causal)}")
+    full_check(w)
+
+
+def test_seqlen_k_zero():
+    w = fa_inputs.make(2, 2, 2, 100, 0, 128, causal=False, seed=60, name="sk0")
+    o, lse = gpu_run(w)
+    assert np.all(o == 0.0) and np.all(lse == -np.inf)
+
+
+def test_large_q_magnitude():
+    w = fa_inputs.make(1, 4, 4, 256, 256, 128, causal=True, seed=61, q_mult=50.0, name="q_x50")
+    full_check(w)
+
+
+def test_gqa_equals_repeated_mha_on_gpu():
+    w = fa_inputs.make(1, 8, 2, 257, 257, 128, causal=True, seed=62, name="gqa")
+    o1, l1 = gpu_run(w)
+    w2 = fa_inputs.make(1, 8, 2, 257, 257, 128, causal=True, seed=62, name="gqa_as_mha")
+    w2.k = w.k.repeat_interleave(4, dim=1).contiguous()
+    w2.v = w.v.repeat_interleave(4, dim=1).contiguous()
+    w2.heads_kv = 8
+    o2, l2 = gpu_run(w2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_deterministic():
+    w = fa_inputs.make(2, 8, 2, 700, 700, 128, causal=True, seed=63, name="det")
+    t = to_device(w)
+    o1, l1 = gpu_run(w, t)
+    o2, l2 = gpu_run(w, t)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_no_writes_outside_outputs():
+    """Outputs carved from larger buffers filled with a sentinel: nothing past the ends changes."""
+    import exact_attention_forward_fa_amd as fa
+
+    lens = [(130, 70), (5, 300), (257, 257)]
+    w = fa_inputs.make(0, 4, 2, 0, 0, 128, causal=True, seed=64, lengths=lens, name="canary")
+    q, k, v, cu, _ = to_device(w)
+    pad = 4096
+    obuf = torch.full((w.total_q * 4 * 128 + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((4 * w.total_q + 2 * pad,), 7.0, dtype=torch.float32, device="cuda")
+    o = obuf[pad:pad + w.total_q * 4 * 128].view(w.total_q, 4, 128)
+    lse = lbuf[pad:pad + 4 * w.total_q].view(4, w.total_q)
+    say("[gpu] fa_fwd canary")
+    fa.forward(q, k, v, causal=True, softmax_scale=w.softmax_scale, cu_seqlens=cu,
+               max_seqlen_q=w.seqlen_q, max_seqlen_k=w.seqlen_k, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:pad] == 7.0) and torch.all(obuf[-pad:] == 7.0)
+    assert torch.all(lbuf[:pad] == 7.0) and torch.all(lbuf[-pad:] == 7.0)
+    ro, rl = oracle_full(w)
+    compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, "bf16", w.name)
