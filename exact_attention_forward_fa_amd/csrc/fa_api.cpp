@@ -126,6 +126,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                    head_dim, head_dim_v, causal, nullptr, &plan);
   if (rc) return rc;
   if (plan.num_workgroups > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  // The kernel addresses one sequence's K or V through a buffer resource
+  // whose byte range is a 31-bit quantity.
+  const int64_t elem = dtype == FA_DTYPE_E4M3 ? 1 : 2;
+  if ((int64_t)seqlen_k * heads_kv * head_dim * elem >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
   if (plan.num_workgroups == 0) return FA_OK;  // no query rows: nothing to write
   fa::Launch L;
   L.p.q = q;

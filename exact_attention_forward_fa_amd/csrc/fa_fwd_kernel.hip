@@ -83,17 +83,52 @@ __device__ __forceinline__ SeqInfo seq_info(const Params& p, int b) {
   return s;
 }
 
+// A row max may grow by up to 2^kLazy (in exp2 units) before O and l are
+// rescaled: P then stays <= 2^kLazy, and O / l is unchanged because both are
+// taken relative to the same stale maximum.
+constexpr float kLazy = 8.f;
+
+// Buffer resource word 3 for raw (untyped, unswizzled) gfx9 buffer loads.
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+// LDS layout of a 64-key block (K or V): 64 rows of D*2 bytes, no padding.
+// 16-byte column `lc` of row `r` is stored at physical column lc ^ swz(r):
+//  * K rows are read 16 B per lane by 16 consecutive rows at one column per
+//    LDS cycle, so swz_k makes those 16 rows hit 16 different 16-byte bank
+//    groups (256 B = all 64 banks);
+//  * V rows are read by the transposing 8-byte loads, four consecutive rows x
+//    64 contiguous bytes per half-wave, so swz_v spreads the four rows over
+//    the four 64-byte quarters of the bank space.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(Params p) {
   constexpr int TM = kTileM, TN = kTileN;
-  constexpr int KP = k_lds_pitch(D), VP = v_lds_pitch(D);
-  constexpr int KBUF = TN * KP, VBUF = TN * VP;
-  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
-  constexpr int NCH = TN * CPR / 256;        // chunks per thread per tile
+  constexpr int RB = D * 2;                  // bytes per K/V row in LDS
+  constexpr int BUF = TN * RB;               // bytes per K or V block buffer
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int NI = TN * CPR / 256;         // direct-load instructions per wave per block
   constexpr int KC = D / 16;                 // k-chunks of the QK^T product
   constexpr int DT = D / 32;                 // 32-wide output tiles of O^T
-  __shared__ __attribute__((aligned(16))) char smem[kStages * (KBUF + VBUF)];
+  // LDS: K buffers [2][TN rows], then V buffers [2][TN rows]
+  __shared__ __attribute__((aligned(1024))) char smem[4 * BUF];
+  char* const kbuf0 = smem;
+  char* const vbuf0 = smem + 2 * BUF;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -116,8 +151,6 @@ void fa_fwd_bf16_kernel(Params p) {
   const bool qvalid = qi < si.sq;
 
   const __bf16* __restrict__ Q = (const __bf16*)p.q;
-  const __bf16* __restrict__ K = (const __bf16*)p.k;
-  const __bf16* __restrict__ V = (const __bf16*)p.v;
   __bf16* __restrict__ O = (__bf16*)p.o;
   const float c = p.scale_log2;
 
@@ -130,7 +163,7 @@ void fa_fwd_bf16_kernel(Params p) {
   const int64_t orow = ((int64_t)(si.q0 + qi) * p.hq + head) * D;
   const int64_t lse_idx = (int64_t)head * si.total_q + si.q0 + qi;
 
-  if (nblk == 0) {  // no admissible key for any row of the tile
+  if (nblk == 0) {  // no admissible key for any row of the tile: store_zero
     if (qvalid) {
       for (int e = hf * 4; e < D; e += 8) *(u32x2*)(O + orow + e) = u32x2{0u, 0u};
       if (hf == 0) p.lse[lse_idx] = -INFINITY;
@@ -149,31 +182,75 @@ void fa_fwd_bf16_kernel(Params p) {
     }
   }
 
-  // ---- K/V block staging: global -> registers -> LDS
-  u32x4 kreg[NCH], vreg[NCH];
-  auto load_tile = [&](int n) {
+  // ---- K/V staging: buffer loads straight into LDS.  Wave w's instruction u
+  // fills the 1 KiB at chunk positions P = (w*NI + u)*64 + lane: row P/CPR,
+  // physical column P%CPR.  The lane fetches the logical column that belongs
+  // there (and, for K, the key the row holds: bits 2 and 3 of the row index
+  // swapped, see k_lds_row).  Keys past the sequence end lie beyond the
+  // resource's num_records and arrive as zeros.
+  const int key_stride_b = p.hkv * D * 2;  // bytes between consecutive keys
+  const char* kseq = (const char*)p.k + ((int64_t)si.k0 * p.hkv + g) * D * 2;
+  const char* vseq = (const char*)p.v + ((int64_t)si.k0 * p.hkv + g) * D * 2;
+  unsigned koff[NI], voff[NI];
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int ch = tid + 256 * u;
-      const int row = ch / CPR, col = ch % CPR;
-      const int key = n * TN + row;
-      const bool ok = key < si.sk;
-      const int64_t off = ((int64_t)(si.k0 + key) * p.hkv + g) * D + col * 8;
-      kreg[u] = ok ? *(const u32x4*)(K + off) : u32x4{0u, 0u, 0u, 0u};
-      vreg[u] = ok ? *(const u32x4*)(V + off) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* kb = smem + buf * (KBUF + VBUF);
-    char* vb = kb + KBUF;
+  for (int u = 0; u < NI; ++u) {
+    const int P = (wave * NI + u) * 64 + lane;
+    const int row = P / CPR, pc = P % CPR;
+    koff[u] = (unsigned)(k_lds_row(row) * key_stride_b + ((pc ^ swz_k<D>(row)) * 16));
+    voff[u] = (unsigned)(row * key_stride_b + ((pc ^ swz_v<D>(row)) * 16));
+  }
+  auto stage = [&](const char* seq, const unsigned* off, char* dst, int n) {
+    const int keys_left = si.sk - n * TN;  // > 0 for every staged block
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(seq + (int64_t)n * TN * key_stride_b), (short)0, keys_left * key_stride_b,
+        kRsrcWord3);
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int ch = tid + 256 * u;
-      const int row = ch / CPR, col = ch % CPR;
-      *(u32x4*)(kb + k_lds_row(row) * KP + col * 16) = kreg[u];
-      *(u32x4*)(vb + row * VP + col * 16) = vreg[u];
-    }
+    for (int u = 0; u < NI; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * NI + u) * 1024), 16,
+                                               off[u], 0, 0, 0);
   };
+  auto stage_k = [&](int n, int buf) { stage(kseq, koff, kbuf0 + buf * BUF, n); };
+  auto stage_v = [&](int n, int buf) { stage(vseq, voff, vbuf0 + buf * BUF, n); };
+
+  // K operand reads: lane (r32, hf) reads row 32t + r32, logical column
+  // 2kc + hf of the K buffer.
+  int ka[KC];
+  {
+    const int x = swz_k<D>(r32);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) ka[kc] = r32 * RB + (((2 * kc + hf) ^ x) * 16);
+  }
+  auto qk = [&](int buf, f32x16* s) {
+    const char* kb = kbuf0 + buf * BUF;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s[t] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 a = *(const bf16x8*)(kb + 32 * t * RB + ka[kc]);
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[t], 0, 0, 0);
+      }
+  };
+
+  // Transposed V reads: lane = 16G + i reads 8 bytes of key row kb + i/4 at
+  // dv columns 32dt + 16(G&1) + 4(i&3); after the transpose it holds
+  // V[kb .. kb+3][32dt + 16(G&1) + i], its own A-operand column.  Rows kb are
+  // multiples of 4, so the row's swizzle is swz_v(i/4) (D=128) and the
+  // column part of the address depends only on dt.
+  int va[DT];
+  {
+    const int tr_row = (lane & 15) >> 2;
+    const int lc_lo = ((lane >> 4) & 1) * 2 + ((lane & 3) >> 1);  // 16-B column within 64 B
+    const int half = (lane & 1) * 8;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int lc = 4 * t + lc_lo;
+      // rows kb + tr_row with kb % 4 == 0: (kb + tr_row) & 3 = tr_row, and for
+      // D=64 ((kb + tr_row) >> 1) & 1 = tr_row >> 1
+      va[t] = (8 * hf + tr_row) * RB + ((lc ^ swz_v<D>(tr_row)) * 16) + half;
+    }
+  }
 
   // ---- running softmax state (per lane: one query, half of each key block)
   f32x16 oacc[DT];
@@ -182,43 +259,30 @@ void fa_fwd_bf16_kernel(Params p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // Transposed V reads: lane = 16G + i reads 8 bytes of key row
-  // (kb + i/4) at dv columns 32dt + 16(G&1) + 4(i&3); after the transpose it
-  // holds V[kb .. kb+3][32dt + 16(G&1) + i], i.e. its own A-operand column.
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
+  // Pipeline: block n is consumed in iteration it = nblk-1-n; block j lives
+  // in K/V buffer (nblk-1-j) & 1.  Iteration it computes S of block n-1 under
+  // the softmax of block n, then O += P_n V_n, while the loads of K of block
+  // n-2 and V of block n-1 fly into the buffers whose previous contents were
+  // last read before this iteration's barrier; they are waited for before the
+  // next barrier.
+  f32x16 s_cur[2], s_nxt[2];
+  stage_k(nblk - 1, 0);
+  stage_v(nblk - 1, 0);
+  if (nblk >= 2) stage_k(nblk - 2, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk(0, s_cur);
 
-  load_tile(nblk - 1);
-  store_tile(0);
-  if (nblk >= 2) load_tile(nblk - 2);
-
-  for (int it = 0; it < nblk; ++it) {
+  // One iteration; MORE = there is a next block whose scores are computed here.
+  auto iteration = [&](const int it, auto more_tag) {
+    constexpr bool MORE = decltype(more_tag)::value;
     const int n = nblk - 1 - it;
     const int buf = it & 1;
-    const char* kb = smem + buf * (KBUF + VBUF);
-    const char* vb = kb + KBUF;
     __syncthreads();
+    if (n >= 2) stage_k(n - 2, buf);
+    if (MORE) stage_v(n - 1, buf ^ 1);
 
-    // S^T (two 32-key sub-tiles) = K_n Q^T
-    f32x16 s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = f32x16{};
-      const char* ka = kb + (32 * t + r32) * KP + hf * 16;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        bf16x8 a = *(const bf16x8*)(ka + kc * 32);
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[t], 0, 0, 0);
-      }
-    }
-
-    // stage the next block while this one is consumed
-    if (it + 1 < nblk) {
-      store_tile(buf ^ 1);
-      if (it + 2 < nblk) load_tile(n - 2);
-    }
-
-    // mask: key index of register r of sub-tile t is n*TN + 32t + 16(r/8) + 8hf + r%8
+    // mask: key of register r of sub-tile t is n*TN + 32t + 16(r/8) + 8hf + r%8
     const bool need_mask = (n + 1) * TN > si.sk || (CAUSAL && (n + 1) * TN - 1 > m0 + diag);
     if (need_mask) {
       const int lim = CAUSAL ? min(si.sk - 1, qi + diag) : si.sk - 1;
@@ -227,52 +291,81 @@ void fa_fwd_bf16_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = n * TN + 32 * t + 16 * (r >> 3) + 8 * hf + (r & 7);
-          if (key > lim) s[t][r] = -INFINITY;
+          if (key > lim) s_cur[t][r] = -INFINITY;
         }
     }
 
-    // online softmax, exp2 form
+    // block row max (in-lane, then across the two half-waves)
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[t][r], s_cur[t][r + 1]));
     mx = halfwave_max(mx);
     const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // all masked so far: keep P = 0
-    const float ms = m_use * c;
-    const float alpha = exp2_fast(m_run * c - ms);
-    m_run = m_new;
+    // lazy rescale: only when some row's max grew by more than 2^kLazy
+    // (m_run = -inf and a finite m_new gives +inf > kLazy; both -inf give NaN)
+    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy)) {
+      // 0 when m_run = -inf < m_new; rows whose max is still -inf hold O = 0
+      // and l = 0 and keep them (their alpha would be exp2(NaN))
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+    }
+    const float ms = (m_run == -INFINITY ? 0.f : m_run) * c;
+
+    // P = exp2(c*S - c*m), row sum, bf16 B operands -- interleaved with the
+    // MFMAs of the next block's scores
     float rs = 0.f;
     bf16x8 pb[4];
+    const char* kb = kbuf0 + (buf ^ 1) * BUF;
+    if (MORE) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) s_nxt[t] = f32x16{};
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -ms));
-        rs += pv;
-        pb[2 * t + (r >> 3)][r & 7] = (__bf16)pv;
+    for (int step = 0; step < 16; ++step) {
+      const int kc = step >> 1, t = step & 1;
+      if (MORE && kc < KC) {
+        bf16x8 a = *(const bf16x8*)(kb + 32 * t * RB + ka[kc]);
+        s_nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_nxt[t], 0, 0, 0);
       }
-    l_run = l_run * alpha + rs;
 #pragma unroll
-    for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      for (int e = 0; e < 2; ++e) {  // two of this lane's 32 scores per step
+        const int idx = 2 * step + e;
+        const int tt = idx >> 4, r = idx & 15;
+        const float pv = exp2_fast(__builtin_fmaf(s_cur[tt][r], c, -ms));
+        rs += pv;
+        pb[2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
+      }
+    }
+    l_run += rs;
 
     // O^T += V_n^T P^T
+    const char* vb = vbuf0 + buf * BUF;
 #pragma unroll
     for (int kc2 = 0; kc2 < 4; ++kc2) {
-      const char* vr = vb + (16 * kc2 + 8 * hf + tr_row) * VP + tr_col;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vr + t * 64));
+            (__attribute__((address_space(3))) i16x4*)(vb + 16 * kc2 * RB + va[t]));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vr + 4 * VP + t * 64));
+            (__attribute__((address_space(3))) i16x4*)(vb + (16 * kc2 + 4) * RB + va[t]));
         bf16x4 lob = __builtin_bit_cast(bf16x4, lo), hib = __builtin_bit_cast(bf16x4, hi);
         bf16x8 a = {lob[0], lob[1], lob[2], lob[3], hib[0], hib[1], hib[2], hib[3]};
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], oacc[t], 0, 0, 0);
       }
     }
-  }
+    if (MORE) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s_cur[t] = s_nxt[t];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  for (int it = 0; it < nblk - 1; ++it) iteration(it, BoolTag<true>{});
+  iteration(nblk - 1, BoolTag<false>{});
 
   // ---- epilogue: normalise, O (bf16) and LSE (natural log)
   const float l_tot = halfwave_sum(l_run);

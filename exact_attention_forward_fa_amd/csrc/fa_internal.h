@@ -12,15 +12,9 @@ constexpr int kTileN = 64;   // keys per main-loop step
 constexpr int kWaves = 4;    // wavefronts per workgroup
 constexpr int kStages = 2;   // K/V LDS buffers
 
-// LDS row pitch (bytes) of the K and V tiles.  K rows are read 16 B per lane
-// by 16 consecutive rows per LDS cycle, so the pitch is an odd multiple of
-// 16 B; V rows are read by the transposing 8 B loads four rows at a time, so
-// the pitch is 64 B mod 256 B and four consecutive rows cover all 64 banks.
-constexpr int k_lds_pitch(int d) { return d * 2 + 16; }
-constexpr int v_lds_pitch(int d) { return d * 2 + 64; }
-constexpr int64_t lds_bytes(int d) {
-  return (int64_t)kStages * kTileN * (k_lds_pitch(d) + v_lds_pitch(d));
-}
+// LDS per workgroup: K and V blocks of kTileN rows of d*2 bytes (no padding;
+// bank conflicts are avoided by swizzling 16-byte columns), double-buffered.
+constexpr int64_t lds_bytes(int d) { return (int64_t)kStages * 2 * kTileN * d * 2; }
 
 struct Params {
   const void* q;

@@ -165,7 +165,7 @@ def test_plan_gfx950():
 
 
 def test_plan_reports_unsupported_when_nothing_fits():
-    small = fa.DeviceLimits(lds_bytes_per_block=64 * KIB, lds_bytes_per_cu=64 * KIB, num_cus=1,
+    small = fa.DeviceLimits(lds_bytes_per_block=48 * KIB, lds_bytes_per_cu=48 * KIB, num_cus=1,
                             simds_per_cu=4, regs_per_simd_lane=512, max_waves_per_simd=8)
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 4, 4, 1024, 1024, False, 128, 128, True, small)
