@@ -46,7 +46,7 @@ class Plan(ctypes.Structure):
                 ("kv_stages", ctypes.c_int), ("lds_bytes", ctypes.c_int64),
                 ("wg_per_cu", ctypes.c_int), ("vgprs_per_lane", ctypes.c_int),
                 ("num_workgroups", ctypes.c_int64), ("m_tiles", ctypes.c_int),
-                ("kernel_variant", ctypes.c_int)]
+                ("kernel_variant", ctypes.c_int), ("query_tiles", ctypes.c_int)]
 
 
 def library_path() -> str:

@@ -85,24 +85,30 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   if (L.lds_bytes_per_block <= 0 || L.lds_bytes_per_cu <= 0 || L.simds_per_cu <= 0 ||
       L.regs_per_simd_lane <= 0)
     return FA_ERR_INVALID;
-  // The compiled kernel: 128 query rows (4 waves x 32), 64-key blocks, K/V
-  // double-buffered in LDS with padded rows, Q in registers, 256 VGPR+AGPR
-  // per lane (2 waves per SIMD).
+  // The compiled kernel: 128 query rows per workgroup (4 waves x 32 rows, Q
+  // in registers), 64-key blocks, K/V double-buffered in LDS without padding,
+  // 256 VGPRs per lane (2 waves per SIMD).
   const int64_t lds = fa::lds_bytes(head_dim);
   if (lds > L.lds_bytes_per_block) return FA_ERR_UNSUPPORTED;
+  const int64_t pairs = (int64_t)batch * heads_kv;
+  const int64_t rounds = (pairs + fa::kXcds - 1) / fa::kXcds;
+  const int qt = 1;
   const int vgprs = 256;
   const int by_lds = (int)(L.lds_bytes_per_cu / lds);
-  const int waves_per_simd_by_regs = L.regs_per_simd_lane / vgprs;
-  const int by_regs = waves_per_simd_by_regs * L.simds_per_cu / fa::kWaves;
-  out->tile_m = fa::kTileM;
+  const int by_regs = (L.regs_per_simd_lane / vgprs) * L.simds_per_cu / fa::kWaves;
+  out->tile_m = fa::kTileM * qt;
   out->tile_n = fa::kTileN;
   out->waves = fa::kWaves;
   out->kv_stages = fa::kStages;
   out->lds_bytes = lds;
   out->wg_per_cu = by_lds < by_regs ? by_lds : by_regs;
   out->vgprs_per_lane = vgprs;
-  out->m_tiles = (seqlen_q + fa::kTileM - 1) / fa::kTileM;
-  out->num_workgroups = (int64_t)out->m_tiles * heads_q * batch;
+  out->query_tiles = qt;
+  out->m_tiles = (seqlen_q + out->tile_m - 1) / out->tile_m;
+  // one slot per (query tile, query head) of every (sequence, kv-head) pair,
+  // the pairs dealt round-robin to the XCDs (the last round padded)
+  out->num_workgroups = out->m_tiles == 0 ? 0
+                        : rounds * fa::kXcds * out->m_tiles * (int64_t)(heads_q / heads_kv);
   out->kernel_variant = (head_dim == 128 ? 0 : 2) + (causal ? 1 : 0) + (dtype == FA_DTYPE_E4M3 ? 4 : 0);
   if (out->wg_per_cu <= 0) return FA_ERR_UNSUPPORTED;
   return FA_OK;
@@ -126,6 +132,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                    head_dim, head_dim_v, causal, nullptr, &plan);
   if (rc) return rc;
   if (plan.num_workgroups > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  const int qt = plan.query_tiles;
   // The kernel addresses one sequence's K or V through a buffer resource
   // whose byte range is a 31-bit quantity.
   const int64_t elem = dtype == FA_DTYPE_E4M3 ? 1 : 2;
@@ -151,6 +158,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   L.causal = causal;
   L.fp8 = dtype == FA_DTYPE_E4M3;
   L.num_workgroups = plan.num_workgroups;
+  L.query_tiles = qt;
   return fa::launch(L, stream);
 }
 

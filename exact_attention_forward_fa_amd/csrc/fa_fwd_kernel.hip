@@ -88,6 +88,14 @@ __device__ __forceinline__ SeqInfo seq_info(const Params& p, int b) {
 // taken relative to the same stale maximum.
 constexpr float kLazy = 8.f;
 
+// Instruction classes of the scheduling hints (LLVM AMDGPU sched_group_barrier
+// masks); the hints only order instructions the compiler already emits.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedTrans = 0x400;
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 // Buffer resource word 3 for raw (untyped, unswizzled) gfx9 buffer loads.
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -136,12 +144,22 @@ void fa_fwd_bf16_kernel(Params p) {
   const int r32 = lane & 31;
   const int hf = lane >> 5;
 
-  // ---- work item: heaviest query tiles first (causal), then (batch, head)
-  const int units = p.hq * p.batch;
-  const int mrev = blockIdx.x / units;
-  const int rest = blockIdx.x - mrev * units;
-  const int head = rest % p.hq;
-  const int b = rest / p.hq;
+  // ---- work item.  Workgroups are dispatched round-robin over the XCDs
+  // (block id mod kXcds), each XCD with its own L2.  The (sequence, kv-head)
+  // pairs are dealt to the XCDs (pair = xcd + kXcds*k), and an XCD works
+  // through its pairs one at a time, heaviest query tiles first, all query
+  // heads of the group side by side -- so the workgroups resident on one XCD
+  // share one pair's K/V in its L2.
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per_pair = p.m_tiles * p.group;
+  const int kk = slot / per_pair;
+  const int within = slot - kk * per_pair;
+  const int pair = xcd + kXcds * kk;
+  if (pair >= p.batch * p.hkv) return;  // padding of the last round
+  const int b = pair / p.hkv;
+  const int mrev = within / p.group;
+  const int head = (pair - b * p.hkv) * p.group + (within - mrev * p.group);
   const int mblk = CAUSAL ? (p.m_tiles - 1 - mrev) : mrev;
   const SeqInfo si = seq_info(p, b);
   const int m0 = mblk * TM;
@@ -199,7 +217,7 @@ void fa_fwd_bf16_kernel(Params p) {
     koff[u] = (unsigned)(k_lds_row(row) * key_stride_b + ((pc ^ swz_k<D>(row)) * 16));
     voff[u] = (unsigned)(row * key_stride_b + ((pc ^ swz_v<D>(row)) * 16));
   }
-  auto stage = [&](const char* seq, const unsigned* off, char* dst, int n) {
+  auto stage = [&](const char* seq, const unsigned* off, char* dst, int n) __attribute__((always_inline)) {
     const int keys_left = si.sk - n * TN;  // > 0 for every staged block
     __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(seq + (int64_t)n * TN * key_stride_b), (short)0, keys_left * key_stride_b,
@@ -209,8 +227,8 @@ void fa_fwd_bf16_kernel(Params p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * NI + u) * 1024), 16,
                                                off[u], 0, 0, 0);
   };
-  auto stage_k = [&](int n, int buf) { stage(kseq, koff, kbuf0 + buf * BUF, n); };
-  auto stage_v = [&](int n, int buf) { stage(vseq, voff, vbuf0 + buf * BUF, n); };
+  auto stage_k = [&](int n, int buf) __attribute__((always_inline)) { stage(kseq, koff, kbuf0 + buf * BUF, n); };
+  auto stage_v = [&](int n, int buf) __attribute__((always_inline)) { stage(vseq, voff, vbuf0 + buf * BUF, n); };
 
   // K operand reads: lane (r32, hf) reads row 32t + r32, logical column
   // 2kc + hf of the K buffer.
@@ -220,7 +238,7 @@ void fa_fwd_bf16_kernel(Params p) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) ka[kc] = r32 * RB + (((2 * kc + hf) ^ x) * 16);
   }
-  auto qk = [&](int buf, f32x16* s) {
+  auto qk = [&](int buf, f32x16* s) __attribute__((always_inline)) {
     const char* kb = kbuf0 + buf * BUF;
 #pragma unroll
     for (int t = 0; t < 2; ++t) s[t] = f32x16{};
@@ -274,7 +292,7 @@ void fa_fwd_bf16_kernel(Params p) {
   qk(0, s_cur);
 
   // One iteration; MORE = there is a next block whose scores are computed here.
-  auto iteration = [&](const int it, auto more_tag) {
+  auto iteration = [&](const int it, auto more_tag) __attribute__((always_inline)) {
     constexpr bool MORE = decltype(more_tag)::value;
     const int n = nblk - 1 - it;
     const int buf = it & 1;

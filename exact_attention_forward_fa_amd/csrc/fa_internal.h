@@ -7,10 +7,11 @@
 namespace fa {
 
 // Kernel geometry shared by the planner and the launcher.
-constexpr int kTileM = 128;  // query rows per workgroup (4 waves x 32 rows)
+constexpr int kTileM = 128;  // query rows per workgroup per query tile (4 waves x 32 rows)
 constexpr int kTileN = 64;   // keys per main-loop step
 constexpr int kWaves = 4;    // wavefronts per workgroup
 constexpr int kStages = 2;   // K/V LDS buffers
+constexpr int kXcds = 8;     // XCDs of an MI355X; workgroups go round-robin over them
 
 // LDS per workgroup: K and V blocks of kTileN rows of d*2 bytes (no padding;
 // bank conflicts are avoided by swizzling 16-byte columns), double-buffered.
@@ -34,6 +35,7 @@ struct Launch {
   int head_dim;
   int causal;
   int fp8;
+  int query_tiles;  // 32-row query tiles per wave (1 or 2)
   int64_t num_workgroups;
 };
 

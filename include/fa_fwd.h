@@ -150,6 +150,7 @@ typedef struct fa_plan {
   int64_t num_workgroups;/* grid size                                         */
   int m_tiles;           /* query tiles per (sequence, head)                  */
   int kernel_variant;    /* index of the compiled kernel                      */
+  int query_tiles;       /* 32-row query tiles per wave (tile_m = 128 * this) */
 } fa_plan_t;
 
 /*

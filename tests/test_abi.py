@@ -161,7 +161,8 @@ def test_plan_gfx950():
     assert p.lds_bytes <= 80 * KIB and p.wg_per_cu == 2
     assert p.m_tiles == 64 and p.num_workgroups == 64 * 32 * 2
     p64 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 2, 2, 256, 256, False, 64, 64, False)
-    assert p64.m_tiles == 2 and p64.num_workgroups == 4 and p64.lds_bytes < p.lds_bytes
+    # 2 (batch, kv-head) pairs dealt to 8 XCDs: one padded round of 8 pairs x 2 tiles x 1 head
+    assert p64.m_tiles == 2 and p64.num_workgroups == 8 * 2 and p64.lds_bytes < p.lds_bytes
 
 
 def test_plan_reports_unsupported_when_nothing_fits():
