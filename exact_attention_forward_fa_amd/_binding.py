@@ -63,7 +63,7 @@ def _load():
 
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is missing: build it with `python -m exact_attention_forward_fa_amd.build` "
+            f"{_LIB_PATH} is missing: build it with `python exact_attention_forward_fa_amd/build.py` "
             "(there is no CPU or PyTorch fallback)")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32 = ctypes.c_void_p, ctypes.c_int

@@ -1,6 +1,8 @@
 """Build libfa_fwd.so (the HIP kernels and the C ABI) for gfx950, in-tree.
 
-    python -m exact_attention_forward_fa_amd.build
+    python exact_attention_forward_fa_amd/build.py
+
+(run by path, not with -m: importing the package loads the library).
 
 hipcc cross-compiles without a GPU.  Packed-FP32 instruction selection is
 switched off for the device code (-packed-fp32-ops).

@@ -88,7 +88,7 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   // The compiled kernel: 128 query rows per workgroup (4 waves x 32 rows, Q
   // in registers), 64-key blocks, K/V double-buffered in LDS without padding,
   // 256 VGPRs per lane (2 waves per SIMD).
-  const int64_t lds = fa::lds_bytes(head_dim);
+  const int64_t lds = fa::lds_bytes(head_dim, dtype == FA_DTYPE_E4M3 ? 1 : 2);
   if (lds > L.lds_bytes_per_block) return FA_ERR_UNSUPPORTED;
   const int64_t pairs = (int64_t)batch * heads_kv;
   const int64_t rounds = (pairs + fa::kXcds - 1) / fa::kXcds;

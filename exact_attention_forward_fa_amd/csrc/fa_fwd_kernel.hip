@@ -106,6 +106,20 @@ struct BoolTag {
   static constexpr bool value = B;
 };
 
+// Pin MFMA results before divergent code.  An MFMA reads operands from all 64
+// lanes; if the compiler sinks one below a branch on a per-lane condition (the
+// epilogue's "row exists" test), the lanes switched off there feed it zeros.
+// An empty asm that consumes the accumulators keeps every MFMA that produces
+// them above this point, under the full execution mask.  (The lambdas that
+// call it are also compiled for the host, where it is empty.)
+template <int N>
+__host__ __device__ __forceinline__ void pin_accumulators(f32x16 (&acc)[N]) {
+#if __HIP_DEVICE_COMPILE__
+#pragma unroll
+  for (int i = 0; i < N; ++i) __asm__ volatile("" : "+v"(acc[i]));
+#endif
+}
+
 // LDS layout of a 64-key block (K or V): 64 rows of D*2 bytes, no padding.
 // 16-byte column `lc` of row `r` is stored at physical column lc ^ swz(r):
 //  * K rows are read 16 B per lane by 16 consecutive rows at one column per
@@ -386,6 +400,7 @@ void fa_fwd_bf16_kernel(Params p) {
   iteration(nblk - 1, BoolTag<false>{});
 
   // ---- epilogue: normalise, O (bf16) and LSE (natural log)
+  pin_accumulators(oacc);
   const float l_tot = halfwave_sum(l_run);
   if (!qvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -399,6 +414,307 @@ void fa_fwd_bf16_kernel(Params p) {
       *(bf16x4*)(O + orow + 32 * t + 8 * i4 + 4 * hf) = ov;
     }
   if (hf == 0) p.lse[lse_idx] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// FP8 (OCP e4m3) inputs.  Same tiling and pipeline as the bf16 kernel, on the
+// gfx950 fp8 MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (block scales fixed at
+// 2^0): each lane feeds 32 bytes of its row (A) or column (B); the 64 products
+// pair A byte (half h, i) with B byte (half h, i), so any assignment of the 64
+// keys (or head-dim entries) to (h, i) that both operands share is valid.
+// Here byte i of half h is key / dim index 32h + i of the 64-wide chunk.
+//  * S^T = K Q^T: K rows from LDS (two 16-byte reads), Q in registers.  The
+//    K rows are placed in LDS so that accumulator register r of half h in
+//    32-key sub-tile t holds key 32h + 16t + r: the exp'd scores are then
+//    already the B operand of the P V product, bytes in key order.
+//  * O^T += V^T P^T with P quantised to e4m3 (P <= 2^kLazy < 448); V^T
+//    arrives through ds_read_b64_tr_b8, which hands lane i of each 16-lane
+//    group column i of an 8-row x 16-byte block.
+//  * The q and k descales fold into the exp2 scale (the forward-pass page's
+//    FP8 branch multiplies softmax_scale_log2 by q_descale * k_descale); the
+//    v descale multiplies O in the epilogue.
+
+// LDS row of a K block (fp8) -> key: row 32t + rho holds key
+// 32((rho>>2)&1) + 16t + 4(rho>>3) + (rho&3), i.e. the key of accumulator
+// register r = 4(rho>>3) + (rho&3) of half (rho>>2)&1 in sub-tile t.
+__device__ __forceinline__ int k8_lds_key(int row) {
+  const int t = row >> 5, rho = row & 31;
+  return 32 * ((rho >> 2) & 1) + 16 * t + 4 * (rho >> 3) + (rho & 3);
+}
+// 16-byte column swizzles of the fp8 K and V blocks (rows of D bytes):
+//  * K: 16 consecutive rows read one column per LDS cycle;
+//  * V: 8 consecutive rows x 32 contiguous bytes per half-wave transposed read.
+template <int D>
+__device__ __forceinline__ int swz_k8(int r) {
+  return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int swz_v8(int r) {
+  return D == 128 ? 2 * ((r >> 1) & 3) : 2 * ((r >> 2) & 1);
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // format 0 (e4m3) for both operands, E8M0 block scales 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_fp8_kernel(Params p) {
+  constexpr int TM = kTileM, TN = kTileN;
+  constexpr int RB = D;                      // bytes per K/V row in LDS
+  constexpr int BUF = TN * RB;               // bytes per K or V block buffer
+  constexpr int CPR = D / 16;                // 16-byte chunks per row
+  constexpr int NI = TN * CPR / 256;         // direct-load instructions per wave per block
+  constexpr int KC = D / 64;                 // 64-wide k-chunks of the QK^T product
+  constexpr int DT = D / 32;                 // 32-wide output tiles of O^T
+  __shared__ __attribute__((aligned(1024))) char smem[4 * BUF];
+  char* const kbuf0 = smem;
+  char* const vbuf0 = smem + 2 * BUF;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r32 = lane & 31;
+  const int hf = lane >> 5;
+
+  // ---- work item (XCD-aware, as in the bf16 kernel)
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per_pair = p.m_tiles * p.group;
+  const int kk = slot / per_pair;
+  const int within = slot - kk * per_pair;
+  const int pair = xcd + kXcds * kk;
+  if (pair >= p.batch * p.hkv) return;
+  const int b = pair / p.hkv;
+  const int mrev = within / p.group;
+  const int head = (pair - b * p.hkv) * p.group + (within - mrev * p.group);
+  const int mblk = CAUSAL ? (p.m_tiles - 1 - mrev) : mrev;
+  const SeqInfo si = seq_info(p, b);
+  const int m0 = mblk * TM;
+  if (m0 >= si.sq) return;
+  const int g = head / p.group;
+  const int qi = m0 + wave * 32 + r32;
+  const bool qvalid = qi < si.sq;
+
+  const unsigned char* __restrict__ Q = (const unsigned char*)p.q;
+  __bf16* __restrict__ O = (__bf16*)p.o;
+  const float dq = p.descales[0], dk = p.descales[1], dvs = p.descales[2];
+  const float c = p.scale_log2 * dq * dk;
+
+  const int diag = si.sk - si.sq;
+  int kend = si.sk;
+  if (CAUSAL) kend = min(kend, m0 + TM + diag);
+  const int nblk = kend > 0 ? (kend + TN - 1) / TN : 0;
+
+  const int64_t qrow = ((int64_t)(si.q0 + qi) * p.hq + head) * D;  // elements of Q and O
+  const int64_t lse_idx = (int64_t)head * si.total_q + si.q0 + qi;
+
+  if (nblk == 0) {  // store_zero
+    if (qvalid) {
+      for (int e = hf * 4; e < D; e += 8) *(u32x2*)(O + qrow + e) = u32x2{0u, 0u};
+      if (hf == 0) p.lse[lse_idx] = -INFINITY;
+    }
+    return;
+  }
+
+  // ---- Q fragments: lane holds Q[qi][64kc + 32hf .. +31]
+  i32x8 qf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const unsigned char* qp = Q + qrow + 64 * kc + 32 * hf;
+    u32x4 lo = qvalid ? *(const u32x4*)qp : u32x4{0u, 0u, 0u, 0u};
+    u32x4 hi = qvalid ? *(const u32x4*)(qp + 16) : u32x4{0u, 0u, 0u, 0u};
+    qf[kc] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+
+  // ---- direct buffer -> LDS staging
+  const int key_stride_b = p.hkv * D;  // bytes between consecutive keys
+  const char* kseq = (const char*)p.k + ((int64_t)si.k0 * p.hkv + g) * D;
+  const char* vseq = (const char*)p.v + ((int64_t)si.k0 * p.hkv + g) * D;
+  unsigned koff[NI], voff[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int P = (wave * NI + u) * 64 + lane;
+    const int row = P / CPR, pc = P % CPR;
+    koff[u] = (unsigned)(k8_lds_key(row) * key_stride_b + ((pc ^ swz_k8<D>(row)) * 16));
+    voff[u] = (unsigned)(row * key_stride_b + ((pc ^ swz_v8<D>(row)) * 16));
+  }
+  auto stage = [&](const char* seq, const unsigned* off, char* dst, int n) __attribute__((always_inline)) {
+    const int keys_left = si.sk - n * TN;
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(seq + (int64_t)n * TN * key_stride_b), (short)0, keys_left * key_stride_b,
+        kRsrcWord3);
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * NI + u) * 1024), 16,
+                                               off[u], 0, 0, 0);
+  };
+  auto stage_k = [&](int n, int buf) __attribute__((always_inline)) { stage(kseq, koff, kbuf0 + buf * BUF, n); };
+  auto stage_v = [&](int n, int buf) __attribute__((always_inline)) { stage(vseq, voff, vbuf0 + buf * BUF, n); };
+
+  // K operand: lane (r32, hf) of sub-tile t reads row 32t + r32, bytes
+  // 64kc + 32hf .. +31 = logical 16-byte columns 4kc + 2hf and 4kc + 2hf + 1
+  int ka[KC][2];
+  {
+    const int x = swz_k8<D>(r32);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) ka[kc][j] = r32 * RB + (((4 * kc + 2 * hf + j) ^ x) * 16);
+  }
+  auto k_operand = [&](const char* kb, int t, int kc) __attribute__((always_inline)) {
+    u32x4 lo = *(const u32x4*)(kb + 32 * t * RB + ka[kc][0]);
+    u32x4 hi = *(const u32x4*)(kb + 32 * t * RB + ka[kc][1]);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto qk = [&](int buf, f32x16* s) __attribute__((always_inline)) {
+    const char* kb = kbuf0 + buf * BUF;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s[t] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[t] = mfma_fp8(k_operand(kb, t, kc), qf[kc], s[t]);
+  };
+
+  // V^T operand of dv tile dt: lane = 16G + 2t' + u reads 8 bytes of key row
+  // 32(G>>1) + 8j + t' at dv columns 32dt + 16(G&1) + 8u (read j = 0..3); the
+  // transpose hands lane i of the group column 32dt + 16(G&1) + i of those 8
+  // rows: bytes 8j .. 8j+7 of its A operand (keys 32h + 8j + 0..7).
+  int va[DT];
+  {
+    const int G = lane >> 4, s16 = lane & 15;
+    const int tr = s16 >> 1, u = s16 & 1;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+      va[t] = (32 * (G >> 1) + tr) * RB + ((((2 * t + (G & 1)) ^ swz_v8<D>(tr)) * 16)) + 8 * u;
+  }
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  f32x16 s_cur[2], s_nxt[2];
+  stage_k(nblk - 1, 0);
+  stage_v(nblk - 1, 0);
+  if (nblk >= 2) stage_k(nblk - 2, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk(0, s_cur);
+
+  auto iteration = [&](const int it, auto more_tag) __attribute__((always_inline)) {
+    constexpr bool MORE = decltype(more_tag)::value;
+    const int n = nblk - 1 - it;
+    const int buf = it & 1;
+    __syncthreads();
+    if (n >= 2) stage_k(n - 2, buf);
+    if (MORE) stage_v(n - 1, buf ^ 1);
+
+    // mask: key of register r of sub-tile t in half hf is n*TN + 32hf + 16t + r
+    const bool need_mask = (n + 1) * TN > si.sk || (CAUSAL && (n + 1) * TN - 1 > m0 + diag);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(si.sk - 1, qi + diag) : si.sk - 1;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (n * TN + 32 * hf + 16 * t + r > lim) s_cur[t][r] = -INFINITY;
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[t][r], s_cur[t][r + 1]));
+    mx = halfwave_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy)) {
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+    }
+    const float ms = (m_run == -INFINITY ? 0.f : m_run) * c;
+
+    // P = exp2(c*S - c*m) -> e4m3 bytes 16t + r of this half's B operand,
+    // under the MFMAs of the next block's scores
+    float rs = 0.f;
+    i32x8 pb;
+    const char* kb = kbuf0 + (buf ^ 1) * BUF;
+    if (MORE) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s_nxt[t] = f32x16{};
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {  // dword w of P: bytes 4w .. 4w+3
+      if (MORE && (w & 1) == 0 && (w >> 1) < 2 * KC) {
+        const int i = w >> 1, kc = i >> 1, t = i & 1;
+        s_nxt[t] = mfma_fp8(k_operand(kb, t, kc), qf[kc], s_nxt[t]);
+      }
+      const int t = w >> 2, r0 = 4 * (w & 3);
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[e] = exp2_fast(__builtin_fmaf(s_cur[t][r0 + e], c, -ms));
+        rs += pv[e];
+      }
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
+      pb[w] = word;
+    }
+    l_run += rs;
+
+    // O^T += V_n^T P^T
+    const char* vb = vbuf0 + buf * BUF;
+    i32x8 va_op[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vb + va[t]));
+      i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vb + 8 * RB + va[t]));
+      i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vb + 16 * RB + va[t]));
+      i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vb + 24 * RB + va[t]));
+      va_op[t] = i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+    }
+#pragma unroll
+    for (int t = 0; t < DT; ++t) oacc[t] = mfma_fp8(va_op[t], pb, oacc[t]);
+    if (MORE) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s_cur[t] = s_nxt[t];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  for (int it = 0; it < nblk - 1; ++it) iteration(it, BoolTag<true>{});
+  iteration(nblk - 1, BoolTag<false>{});
+
+  pin_accumulators(oacc);
+  const float l_tot = halfwave_sum(l_run);
+  if (!qvalid) return;
+  const float inv = l_tot > 0.f ? dvs / l_tot : 0.f;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 ov;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(oacc[t][4 * i4 + j] * inv);
+      *(bf16x4*)(O + qrow + 32 * t + 8 * i4 + 4 * hf) = ov;
+    }
+  if (hf == 0) p.lse[lse_idx] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+template <int D, bool CAUSAL>
+void launch_fp8(const Launch& L, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)L.num_workgroups), dim3(256),
+                     0, stream, L.p);
 }
 
 template <int D, bool CAUSAL>
@@ -427,8 +743,15 @@ int launch(const Launch& L, void* stream_) {
   if (!device_is_gfx950()) return FA_ERR_DEVICE;
   hipStream_t stream = (hipStream_t)stream_;
   (void)hipGetLastError();  // clear a stale error so the check below is ours
-  if (L.fp8) return FA_ERR_UNSUPPORTED;
-  if (L.head_dim == 128) {
+  if (L.fp8) {
+    if (L.head_dim == 128) {
+      if (L.causal) launch_fp8<128, true>(L, stream);
+      else launch_fp8<128, false>(L, stream);
+    } else {
+      if (L.causal) launch_fp8<64, true>(L, stream);
+      else launch_fp8<64, false>(L, stream);
+    }
+  } else if (L.head_dim == 128) {
     if (L.causal) launch_bf16<128, true>(L, stream);
     else launch_bf16<128, false>(L, stream);
   } else {

@@ -15,7 +15,9 @@ constexpr int kXcds = 8;     // XCDs of an MI355X; workgroups go round-robin ove
 
 // LDS per workgroup: K and V blocks of kTileN rows of d*2 bytes (no padding;
 // bank conflicts are avoided by swizzling 16-byte columns), double-buffered.
-constexpr int64_t lds_bytes(int d) { return (int64_t)kStages * 2 * kTileN * d * 2; }
+constexpr int64_t lds_bytes(int d, int elem_bytes) {
+  return (int64_t)kStages * 2 * kTileN * d * elem_bytes;
+}
 
 struct Params {
   const void* q;

@@ -144,3 +144,29 @@ def test_no_writes_outside_outputs():
     assert torch.all(lbuf[:pad] == 7.0) and torch.all(lbuf[-pad:] == 7.0)
     ro, rl = oracle_full(w)
     compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, "bf16", w.name)
+
+
+# ------------------------------------------------------------------- fp8 e4m3
+
+def test_fp8_causal_16384_sampled():
+    w = fa_inputs.workload("fp8_causal_b1_h32_s16384_d128")
+    o, lse = sampled_check(w, n_random=32)
+    assert np.isfinite(lse).all() and np.isfinite(o).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 4, 4, 300, 300), (1, 8, 2, 200, 517), (1, 4, 1, 517, 200),
+                                   (1, 2, 2, 1, 1)])
+def test_fp8_ragged_shapes(shape, causal, d):
+    b, hq, hkv, sq, sk = shape
+    w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq * 5 + sk + d + 1, dtype="e4m3",
+                       name=f"fp8_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}_c{int(causal)}")
+    full_check(w)
+
+
+def test_fp8_varlen():
+    lens = [(300, 517), (1, 64), (129, 100), (64, 0), (0, 40), (255, 256)]
+    w = fa_inputs.make(0, 4, 2, 0, 0, 128, causal=True, seed=70, lengths=lens, dtype="e4m3",
+                       name="fp8_varlen_small")
+    full_check(w)
