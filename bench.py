@@ -108,17 +108,18 @@ def cpu_baseline(w, target_s: float):
 
     dt = oracle.BF16 if w.dtype == "bf16" else oracle.E4M3
     kw = w.shape_kwargs()
-    # calibrate on a small sample, then size the measured sample to about target_s seconds
-    cal = draw(max(16, oracle.num_threads()))
+    # calibrate on a sample large enough to keep every thread busy (a handful of rows
+    # under-reports the rate: thread start-up and imbalance dominate), then draw rows until the
+    # measured sample holds about target_s seconds of work
+    cal = draw(64 * oracle.num_threads())
     t0 = time.perf_counter()
     oracle.attention_rows(w.q, w.k, w.v, cal, descales=w.descales, dtype=dt, **kw)
     t_cal = time.perf_counter() - t0
     rate = flops / max(t_cal, 1e-6)
     flops = 0
-    n = 16
-    rows = draw(n)
-    while flops < rate * target_s and len(rows) < 1_000_000:
-        rows += draw(len(rows))
+    rows = []
+    while flops < rate * target_s and len(rows) < 2_000_000:
+        rows += draw(256)
     t0 = time.perf_counter()
     oracle.attention_rows(w.q, w.k, w.v, rows, descales=w.descales, dtype=dt, **kw)
     sec = time.perf_counter() - t0
