@@ -42,11 +42,32 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum that propagates NaN (IEEE 754-2019 maximum).  Scores are never NaN
+// here; unlike fmaxf it needs no quieting of its inputs, and chains of it map
+// onto v_maximum3_f32.
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Maximum of the 32 scores a lane holds for one key block (two 16-register
+// accumulators), as four independent chains of three-input maxima.
+__device__ __forceinline__ float block_max(const f32x16 (&s)[2]) {
+  float ch[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x16& v = s[q >> 1];
+    const int r0 = 8 * (q & 1);
+    float m = fmax_nan(v[r0], v[r0 + 1]);
+#pragma unroll
+    for (int j = 2; j < 8; j += 2) m = fmax_nan(fmax_nan(m, v[r0 + j]), v[r0 + j + 1]);
+    ch[q] = m;
+  }
+  return fmax_nan(fmax_nan(ch[0], ch[1]), fmax_nan(ch[2], ch[3]));
+}
+
 // max / sum of a value over lanes l and l^32 (the two half-waves hold the
 // same 32 queries): permlane32_swap returns {own, partner} in some order.
 __device__ __forceinline__ float halfwave_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halfwave_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -100,11 +121,6 @@ constexpr int kSchedTrans = 0x400;
 constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) void lds_void;
-
-template <bool B>
-struct BoolTag {
-  static constexpr bool value = B;
-};
 
 // Pin MFMA results before divergent code.  An MFMA reads operands from all 64
 // lanes; if the compiler sinks one below a branch on a per-lane condition (the
@@ -296,23 +312,32 @@ void fa_fwd_bf16_kernel(Params p) {
   // the softmax of block n, then O += P_n V_n, while the loads of K of block
   // n-2 and V of block n-1 fly into the buffers whose previous contents were
   // last read before this iteration's barrier; they are waited for before the
-  // next barrier.
-  f32x16 s_cur[2], s_nxt[2];
+  // next barrier.  Iterations come in pairs (even it: buffer 0 is consumed,
+  // odd: buffer 1), so the buffer addresses are constants and the two score
+  // arrays swap roles instead of being copied.  The last iteration (n = 0)
+  // also computes a score tile, from a stale K buffer, that nothing reads:
+  // this keeps one copy of the loop body per buffer parity (a separate last
+  // iteration made the register allocator spill).
+  f32x16 s_a[2], s_b[2];
   stage_k(nblk - 1, 0);
   stage_v(nblk - 1, 0);
   if (nblk >= 2) stage_k(nblk - 2, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  qk(0, s_cur);
+  qk(0, s_a);
 
-  // One iteration; MORE = there is a next block whose scores are computed here.
-  auto iteration = [&](const int it, auto more_tag) __attribute__((always_inline)) {
-    constexpr bool MORE = decltype(more_tag)::value;
+  // One iteration.  sc: scores of block n; sn: receives those of block n-1
+  // (unused when n = 0).  The four LDS regions are distinct
+  // within an iteration (K and V being read, K and V being loaded); the
+  // __restrict__ qualifiers tell the compiler so, which keeps it from waiting
+  // for the in-flight buffer->LDS loads before the transposed V reads.
+  auto iteration = [&](const int it, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                       const char* __restrict__ kread, const char* __restrict__ vread,
+                       char* __restrict__ kdst, char* __restrict__ vdst) __attribute__((always_inline)) {
     const int n = nblk - 1 - it;
-    const int buf = it & 1;
     __syncthreads();
-    if (n >= 2) stage_k(n - 2, buf);
-    if (MORE) stage_v(n - 1, buf ^ 1);
+    if (n >= 2) stage(kseq, koff, kdst, n - 2);
+    if (n >= 1) stage(vseq, voff, vdst, n - 1);
 
     // mask: key of register r of sub-tile t is n*TN + 32t + 16(r/8) + 8hf + r%8
     const bool need_mask = (n + 1) * TN > si.sk || (CAUSAL && (n + 1) * TN - 1 > m0 + diag);
@@ -323,18 +348,12 @@ void fa_fwd_bf16_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = n * TN + 32 * t + 16 * (r >> 3) + 8 * hf + (r & 7);
-          if (key > lim) s_cur[t][r] = -INFINITY;
+          if (key > lim) sc[t][r] = -INFINITY;
         }
     }
 
     // block row max (in-lane, then across the two half-waves)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[t][r], s_cur[t][r + 1]));
-    mx = halfwave_max(mx);
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
     // lazy rescale: only when some row's max grew by more than 2^kLazy
     // (m_run = -inf and a finite m_new gives +inf > kLazy; both -inf give NaN)
     if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy)) {
@@ -352,23 +371,20 @@ void fa_fwd_bf16_kernel(Params p) {
     // MFMAs of the next block's scores
     float rs = 0.f;
     bf16x8 pb[4];
-    const char* kb = kbuf0 + (buf ^ 1) * BUF;
-    if (MORE) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) s_nxt[t] = f32x16{};
-    }
+    for (int t = 0; t < 2; ++t) sn[t] = f32x16{};
 #pragma unroll
     for (int step = 0; step < 16; ++step) {
       const int kc = step >> 1, t = step & 1;
-      if (MORE && kc < KC) {
-        bf16x8 a = *(const bf16x8*)(kb + 32 * t * RB + ka[kc]);
-        s_nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_nxt[t], 0, 0, 0);
+      if (kc < KC) {
+        bf16x8 a = *(const bf16x8*)(kread + 32 * t * RB + ka[kc]);
+        sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], sn[t], 0, 0, 0);
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e) {  // two of this lane's 32 scores per step
         const int idx = 2 * step + e;
         const int tt = idx >> 4, r = idx & 15;
-        const float pv = exp2_fast(__builtin_fmaf(s_cur[tt][r], c, -ms));
+        const float pv = exp2_fast(__builtin_fmaf(sc[tt][r], c, -ms));
         rs += pv;
         pb[2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
       }
@@ -376,28 +392,32 @@ void fa_fwd_bf16_kernel(Params p) {
     l_run += rs;
 
     // O^T += V_n^T P^T
-    const char* vb = vbuf0 + buf * BUF;
 #pragma unroll
     for (int kc2 = 0; kc2 < 4; ++kc2) {
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + 16 * kc2 * RB + va[t]));
+            (__attribute__((address_space(3))) i16x4*)(vread + 16 * kc2 * RB + va[t]));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + (16 * kc2 + 4) * RB + va[t]));
+            (__attribute__((address_space(3))) i16x4*)(vread + (16 * kc2 + 4) * RB + va[t]));
         bf16x4 lob = __builtin_bit_cast(bf16x4, lo), hib = __builtin_bit_cast(bf16x4, hi);
         bf16x8 a = {lob[0], lob[1], lob[2], lob[3], hib[0], hib[1], hib[2], hib[3]};
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], oacc[t], 0, 0, 0);
       }
     }
-    if (MORE) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) s_cur[t] = s_nxt[t];
-    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  for (int it = 0; it < nblk - 1; ++it) iteration(it, BoolTag<true>{});
-  iteration(nblk - 1, BoolTag<false>{});
+  // even iterations consume buffer 0 and load into K buffer 0 / V buffer 1;
+  // odd iterations the other way round
+  char* const k0b = kbuf0;
+  char* const k1b = kbuf0 + BUF;
+  char* const v0b = vbuf0;
+  char* const v1b = vbuf0 + BUF;
+  for (int it = 0; it < nblk; it += 2) {
+    iteration(it, s_a, s_b, k1b, v0b, k0b, v1b);
+    if (it + 1 == nblk) break;
+    iteration(it + 1, s_b, s_a, k0b, v1b, k1b, v0b);
+  }
 
   // ---- epilogue: normalise, O (bf16) and LSE (natural log)
   pin_accumulators(oacc);
@@ -602,21 +622,22 @@ void fa_fwd_fp8_kernel(Params p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  f32x16 s_cur[2], s_nxt[2];
+  // Pipeline, buffer rotation and iteration pairs as in the bf16 kernel.
+  f32x16 s_a[2], s_b[2];
   stage_k(nblk - 1, 0);
   stage_v(nblk - 1, 0);
   if (nblk >= 2) stage_k(nblk - 2, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  qk(0, s_cur);
+  qk(0, s_a);
 
-  auto iteration = [&](const int it, auto more_tag) __attribute__((always_inline)) {
-    constexpr bool MORE = decltype(more_tag)::value;
+  auto iteration = [&](const int it, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                       const char* __restrict__ kread, const char* __restrict__ vread,
+                       char* __restrict__ kdst, char* __restrict__ vdst) __attribute__((always_inline)) {
     const int n = nblk - 1 - it;
-    const int buf = it & 1;
     __syncthreads();
-    if (n >= 2) stage_k(n - 2, buf);
-    if (MORE) stage_v(n - 1, buf ^ 1);
+    if (n >= 2) stage(kseq, koff, kdst, n - 2);
+    if (n >= 1) stage(vseq, voff, vdst, n - 1);
 
     // mask: key of register r of sub-tile t in half hf is n*TN + 32hf + 16t + r
     const bool need_mask = (n + 1) * TN > si.sk || (CAUSAL && (n + 1) * TN - 1 > m0 + diag);
@@ -626,16 +647,10 @@ void fa_fwd_fp8_kernel(Params p) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (n * TN + 32 * hf + 16 * t + r > lim) s_cur[t][r] = -INFINITY;
+          if (n * TN + 32 * hf + 16 * t + r > lim) sc[t][r] = -INFINITY;
     }
 
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[t][r], s_cur[t][r + 1]));
-    mx = halfwave_max(mx);
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
     if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy)) {
       const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
       m_run = m_new;
@@ -649,22 +664,19 @@ void fa_fwd_fp8_kernel(Params p) {
     // under the MFMAs of the next block's scores
     float rs = 0.f;
     i32x8 pb;
-    const char* kb = kbuf0 + (buf ^ 1) * BUF;
-    if (MORE) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) s_nxt[t] = f32x16{};
-    }
+    for (int t = 0; t < 2; ++t) sn[t] = f32x16{};
 #pragma unroll
     for (int w = 0; w < 8; ++w) {  // dword w of P: bytes 4w .. 4w+3
-      if (MORE && (w & 1) == 0 && (w >> 1) < 2 * KC) {
+      if ((w & 1) == 0 && (w >> 1) < 2 * KC) {
         const int i = w >> 1, kc = i >> 1, t = i & 1;
-        s_nxt[t] = mfma_fp8(k_operand(kb, t, kc), qf[kc], s_nxt[t]);
+        sn[t] = mfma_fp8(k_operand(kread, t, kc), qf[kc], sn[t]);
       }
       const int t = w >> 2, r0 = 4 * (w & 3);
       float pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pv[e] = exp2_fast(__builtin_fmaf(s_cur[t][r0 + e], c, -ms));
+        pv[e] = exp2_fast(__builtin_fmaf(sc[t][r0 + e], c, -ms));
         rs += pv[e];
       }
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
@@ -674,26 +686,28 @@ void fa_fwd_fp8_kernel(Params p) {
     l_run += rs;
 
     // O^T += V_n^T P^T
-    const char* vb = vbuf0 + buf * BUF;
     i32x8 va_op[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vb + va[t]));
-      i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vb + 8 * RB + va[t]));
-      i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vb + 16 * RB + va[t]));
-      i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vb + 24 * RB + va[t]));
+      i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vread + va[t]));
+      i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vread + 8 * RB + va[t]));
+      i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vread + 16 * RB + va[t]));
+      i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vread + 24 * RB + va[t]));
       va_op[t] = i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
     }
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[t] = mfma_fp8(va_op[t], pb, oacc[t]);
-    if (MORE) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) s_cur[t] = s_nxt[t];
-    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  for (int it = 0; it < nblk - 1; ++it) iteration(it, BoolTag<true>{});
-  iteration(nblk - 1, BoolTag<false>{});
+  char* const k0b = kbuf0;
+  char* const k1b = kbuf0 + BUF;
+  char* const v0b = vbuf0;
+  char* const v1b = vbuf0 + BUF;
+  for (int it = 0; it < nblk; it += 2) {
+    iteration(it, s_a, s_b, k1b, v0b, k0b, v1b);
+    if (it + 1 == nblk) break;
+    iteration(it + 1, s_b, s_a, k0b, v1b, k1b, v0b);
+  }
 
   pin_accumulators(oacc);
   const float l_tot = halfwave_sum(l_run);
