@@ -7,7 +7,8 @@ through ctypes.  The names mirror the C ABI in ``include/fa_fwd.h``:
     fa_fwd(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
            cu_seqlens, head_dim, head_dim_v, softmax_scale, causal, descales,
            stream=None)
-    fa_fwd_plan(...), fa_smem_screen(...), fa_gfx950_limits(), fa_strerror(code)
+    fa_fwd_plan(...), fa_smem_screen(...), fa_gfx950_limits(), fa_strerror(code),
+    fa_set_query_tiles(n)
 
 ``forward(q, k, v, ...)`` is a convenience that allocates O and LSE with torch
 and calls ``fa_fwd``.  There is no fallback: if the library is missing the
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     TileConfig,
     fa_fwd,
     fa_fwd_plan,
+    fa_set_query_tiles,
     fa_gfx950_limits,
     fa_smem_screen,
     fa_strerror,

@@ -81,6 +81,8 @@ def _load():
                                 ctypes.POINTER(DeviceLimits), ctypes.POINTER(Plan)]
     lib.fa_fwd_plan.restype = i32
     lib.fa_version.restype = i32
+    lib.fa_set_query_tiles.argtypes = [i32]
+    lib.fa_set_query_tiles.restype = i32
     return lib
 
 
@@ -93,6 +95,13 @@ def fa_strerror(code: int) -> str:
 
 def fa_version() -> int:
     return int(_lib.fa_version())
+
+
+def fa_set_query_tiles(query_tiles: int) -> None:
+    """Tuning override of the bf16 tiling: 0 automatic, 1 or 2 query tiles of 32 rows per wave."""
+    rc = _lib.fa_set_query_tiles(int(query_tiles))
+    if rc != 0:
+        raise FaError(rc, "fa_set_query_tiles")
 
 
 def fa_gfx950_limits() -> DeviceLimits:

@@ -7,12 +7,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/fa_fwd.h"
 #include "fa_internal.h"
 
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+
+// fa_set_query_tiles: 0 automatic, else the forced bf16 query tiles per wave
+std::atomic<int> g_query_tiles{0};
 
 // gfx950 (MI355X): 160 KiB LDS per CU, all of it addressable by one
 // workgroup; 256 CUs; 4 SIMDs per CU; 512 VGPR+AGPR per lane per SIMD;
@@ -43,6 +48,12 @@ const char* fa_strerror(int code) {
     case FA_ERR_DEVICE: return "device error (not gfx950, or the kernel launch failed)";
     default: return "unknown error code";
   }
+}
+
+int fa_set_query_tiles(int query_tiles) {
+  if (query_tiles < 0 || query_tiles > 2) return FA_ERR_INVALID;
+  g_query_tiles.store(query_tiles, std::memory_order_relaxed);
+  return FA_OK;
 }
 
 int fa_gfx950_limits(fa_device_limits_t* out) {
@@ -85,15 +96,22 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   if (L.lds_bytes_per_block <= 0 || L.lds_bytes_per_cu <= 0 || L.simds_per_cu <= 0 ||
       L.regs_per_simd_lane <= 0)
     return FA_ERR_INVALID;
-  // The compiled kernel: 128 query rows per workgroup (4 waves x 32 rows, Q
-  // in registers), 64-key blocks, K/V double-buffered in LDS without padding,
-  // 256 VGPRs per lane (2 waves per SIMD).
+  // The compiled kernels: 4 waves per workgroup, each wave holding QT query
+  // tiles of 32 rows (Q in registers), 64-key blocks, K/V double-buffered in
+  // LDS without padding.  QT = 1: 128 rows per workgroup, 256 registers per
+  // lane (2 waves per SIMD).  QT = 2 (bf16): 256 rows per workgroup, the full
+  // 512-register file (1 wave per SIMD); each LDS operand read feeds two
+  // MFMAs.  The automatic choice is QT = 1 (measured faster on every
+  // workload so far: with one wave per SIMD nothing hides the softmax's
+  // serial steps); QT = 2 is reachable through fa_set_query_tiles.
   const int64_t lds = fa::lds_bytes(head_dim, dtype == FA_DTYPE_E4M3 ? 1 : 2);
   if (lds > L.lds_bytes_per_block) return FA_ERR_UNSUPPORTED;
   const int64_t pairs = (int64_t)batch * heads_kv;
   const int64_t rounds = (pairs + fa::kXcds - 1) / fa::kXcds;
-  const int qt = 1;
-  const int vgprs = 256;
+  const int forced = g_query_tiles.load(std::memory_order_relaxed);
+  const bool wide_ok = dtype == FA_DTYPE_BF16 && L.regs_per_simd_lane >= 512;
+  const int qt = wide_ok && forced ? forced : 1;
+  const int vgprs = 256 * qt;
   const int by_lds = (int)(L.lds_bytes_per_cu / lds);
   const int by_regs = (L.regs_per_simd_lane / vgprs) * L.simds_per_cu / fa::kWaves;
   out->tile_m = fa::kTileM * qt;

@@ -122,6 +122,11 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 // Pin MFMA results before divergent code.  An MFMA reads operands from all 64
 // lanes; if the compiler sinks one below a branch on a per-lane condition (the
 // epilogue's "row exists" test), the lanes switched off there feed it zeros.
@@ -133,6 +138,16 @@ __host__ __device__ __forceinline__ void pin_accumulators(f32x16 (&acc)[N]) {
 #if __HIP_DEVICE_COMPILE__
 #pragma unroll
   for (int i = 0; i < N; ++i) __asm__ volatile("" : "+v"(acc[i]));
+#endif
+}
+// The same for accumulators that live in AGPRs (kernels that use the full
+// 512-register file): an "a" constraint keeps the register allocator from
+// homing them in VGPRs and copying them across every loop iteration.
+template <int N>
+__host__ __device__ __forceinline__ void pin_accumulators_agpr(f32x16 (&acc)[N]) {
+#if __HIP_DEVICE_COMPILE__
+#pragma unroll
+  for (int i = 0; i < N; ++i) __asm__ volatile("" : "+a"(acc[i]));
 #endif
 }
 
@@ -153,10 +168,16 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// QG = query groups of 32 rows per wave.  QG = 1: 128 rows per workgroup,
+// two workgroups (eight waves) per CU.  QG = 2: 256 rows per workgroup, one
+// wave per SIMD with the full 512-register file; every K operand read and
+// every transposed V read from LDS then feeds two MFMAs instead of one, which
+// halves the LDS traffic per MFMA (the transposed V reads are what limits the
+// QG = 1 tiling).
+template <int D, bool CAUSAL, int QG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QG == 1 ? 2 : 1, QG == 1 ? 2 : 1)))
 void fa_fwd_bf16_kernel(Params p) {
-  constexpr int TM = kTileM, TN = kTileN;
+  constexpr int TM = kTileM * QG, TN = kTileN;
   constexpr int RB = D * 2;                  // bytes per K/V row in LDS
   constexpr int BUF = TN * RB;               // bytes per K or V block buffer
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -195,8 +216,13 @@ void fa_fwd_bf16_kernel(Params p) {
   const int m0 = mblk * TM;
   if (m0 >= si.sq) return;  // uniform over the workgroup, before any barrier
   const int g = head / p.group;
-  const int qi = m0 + wave * 32 + r32;  // this lane's query row in the sequence
-  const bool qvalid = qi < si.sq;
+  int qi[QG];       // this lane's query rows in the sequence (one per group)
+  bool qvalid[QG];
+#pragma unroll
+  for (int q = 0; q < QG; ++q) {
+    qi[q] = m0 + (wave * QG + q) * 32 + r32;
+    qvalid[q] = qi[q] < si.sq;
+  }
 
   const __bf16* __restrict__ Q = (const __bf16*)p.q;
   __bf16* __restrict__ O = (__bf16*)p.o;
@@ -208,25 +234,32 @@ void fa_fwd_bf16_kernel(Params p) {
   if (CAUSAL) kend = min(kend, m0 + TM + diag);
   const int nblk = kend > 0 ? (kend + TN - 1) / TN : 0;
 
-  const int64_t orow = ((int64_t)(si.q0 + qi) * p.hq + head) * D;
-  const int64_t lse_idx = (int64_t)head * si.total_q + si.q0 + qi;
+  int64_t orow[QG], lse_idx[QG];
+#pragma unroll
+  for (int q = 0; q < QG; ++q) {
+    orow[q] = ((int64_t)(si.q0 + qi[q]) * p.hq + head) * D;
+    lse_idx[q] = (int64_t)head * si.total_q + si.q0 + qi[q];
+  }
 
   if (nblk == 0) {  // no admissible key for any row of the tile: store_zero
-    if (qvalid) {
-      for (int e = hf * 4; e < D; e += 8) *(u32x2*)(O + orow + e) = u32x2{0u, 0u};
-      if (hf == 0) p.lse[lse_idx] = -INFINITY;
-    }
+#pragma unroll
+    for (int q = 0; q < QG; ++q)
+      if (qvalid[q]) {
+        for (int e = hf * 4; e < D; e += 8) *(u32x2*)(O + orow[q] + e) = u32x2{0u, 0u};
+        if (hf == 0) p.lse[lse_idx[q]] = -INFINITY;
+      }
     return;
   }
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16kc + 8hf .. +7]
-  bf16x8 qf[KC];
-  {
-    const __bf16* qp = Q + orow + 8 * hf;
+  bf16x8 qf[QG][KC];
+#pragma unroll
+  for (int q = 0; q < QG; ++q) {
+    const __bf16* qp = Q + orow[q] + 8 * hf;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      u32x4 t = qvalid ? *(const u32x4*)(qp + 16 * kc) : u32x4{0u, 0u, 0u, 0u};
-      qf[kc] = __builtin_bit_cast(bf16x8, t);
+      u32x4 t = qvalid[q] ? *(const u32x4*)(qp + 16 * kc) : u32x4{0u, 0u, 0u, 0u};
+      qf[q][kc] = __builtin_bit_cast(bf16x8, t);
     }
   }
 
@@ -247,6 +280,8 @@ void fa_fwd_bf16_kernel(Params p) {
     koff[u] = (unsigned)(k_lds_row(row) * key_stride_b + ((pc ^ swz_k<D>(row)) * 16));
     voff[u] = (unsigned)(row * key_stride_b + ((pc ^ swz_v<D>(row)) * 16));
   }
+  // LDS destination of this wave's first instruction, wave-uniform by construction
+  const int wave_lds = __builtin_amdgcn_readfirstlane(wave * NI * 1024);
   auto stage = [&](const char* seq, const unsigned* off, char* dst, int n) __attribute__((always_inline)) {
     const int keys_left = si.sk - n * TN;  // > 0 for every staged block
     __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -254,7 +289,7 @@ void fa_fwd_bf16_kernel(Params p) {
         kRsrcWord3);
 #pragma unroll
     for (int u = 0; u < NI; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * NI + u) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + wave_lds + u * 1024), 16,
                                                off[u], 0, 0, 0);
   };
   auto stage_k = [&](int n, int buf) __attribute__((always_inline)) { stage(kseq, koff, kbuf0 + buf * BUF, n); };
@@ -268,16 +303,20 @@ void fa_fwd_bf16_kernel(Params p) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) ka[kc] = r32 * RB + (((2 * kc + hf) ^ x) * 16);
   }
-  auto qk = [&](int buf, f32x16* s) __attribute__((always_inline)) {
+  auto qk = [&](int buf, f32x16 (&s)[QG][2]) __attribute__((always_inline)) {
     const char* kb = kbuf0 + buf * BUF;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) s[t] = f32x16{};
+    for (int q = 0; q < QG; ++q)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[q][t] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         bf16x8 a = *(const bf16x8*)(kb + 32 * t * RB + ka[kc]);
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[t], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < QG; ++q)
+          s[q][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[q][kc], s[q][t], 0, 0, 0);
       }
   };
 
@@ -300,12 +339,18 @@ void fa_fwd_bf16_kernel(Params p) {
     }
   }
 
-  // ---- running softmax state (per lane: one query, half of each key block)
-  f32x16 oacc[DT];
+  // ---- running softmax state (per lane and group: one query, half of each key block)
+  f32x16 oacc[QG][DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  for (int q = 0; q < QG; ++q)
+#pragma unroll
+    for (int t = 0; t < DT; ++t) oacc[q][t] = f32x16{};
+  float m_run[QG], l_run[QG];
+#pragma unroll
+  for (int q = 0; q < QG; ++q) {
+    m_run[q] = -INFINITY;
+    l_run[q] = 0.f;
+  }
 
   // Pipeline: block n is consumed in iteration it = nblk-1-n; block j lives
   // in K/V buffer (nblk-1-j) & 1.  Iteration it computes S of block n-1 under
@@ -318,7 +363,7 @@ void fa_fwd_bf16_kernel(Params p) {
   // also computes a score tile, from a stale K buffer, that nothing reads:
   // this keeps one copy of the loop body per buffer parity (a separate last
   // iteration made the register allocator spill).
-  f32x16 s_a[2], s_b[2];
+  f32x16 s_a[QG][2], s_b[QG][2];
   stage_k(nblk - 1, 0);
   stage_v(nblk - 1, 0);
   if (nblk >= 2) stage_k(nblk - 2, 1);
@@ -327,69 +372,99 @@ void fa_fwd_bf16_kernel(Params p) {
   qk(0, s_a);
 
   // One iteration.  sc: scores of block n; sn: receives those of block n-1
-  // (unused when n = 0).  The four LDS regions are distinct
-  // within an iteration (K and V being read, K and V being loaded); the
-  // __restrict__ qualifiers tell the compiler so, which keeps it from waiting
-  // for the in-flight buffer->LDS loads before the transposed V reads.
-  auto iteration = [&](const int it, f32x16 (&sc)[2], f32x16 (&sn)[2],
+  // (unused when n = 0).  The four LDS regions are distinct within an
+  // iteration (K and V being read, K and V being loaded); the __restrict__
+  // qualifiers tell the compiler so, which keeps it from waiting for the
+  // in-flight buffer->LDS loads before the transposed V reads.
+  auto iteration = [&](const int it, f32x16 (&sc)[QG][2], f32x16 (&sn)[QG][2],
                        const char* __restrict__ kread, const char* __restrict__ vread,
-                       char* __restrict__ kdst, char* __restrict__ vdst) __attribute__((always_inline)) {
+                       char* __restrict__ kdst, char* __restrict__ vdst,
+                       auto mask_tag) __attribute__((always_inline)) {
     const int n = nblk - 1 - it;
     __syncthreads();
     if (n >= 2) stage(kseq, koff, kdst, n - 2);
     if (n >= 1) stage(vseq, voff, vdst, n - 1);
 
     // mask: key of register r of sub-tile t is n*TN + 32t + 16(r/8) + 8hf + r%8
-    const bool need_mask = (n + 1) * TN > si.sk || (CAUSAL && (n + 1) * TN - 1 > m0 + diag);
-    if (need_mask) {
-      const int lim = CAUSAL ? min(si.sk - 1, qi + diag) : si.sk - 1;
+    if (decltype(mask_tag)::value) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int q = 0; q < QG; ++q) {
+        const int lim = CAUSAL ? min(si.sk - 1, qi[q] + diag) : si.sk - 1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n * TN + 32 * t + 16 * (r >> 3) + 8 * hf + (r & 7);
-          if (key > lim) sc[t][r] = -INFINITY;
-        }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = n * TN + 32 * t + 16 * (r >> 3) + 8 * hf + (r & 7);
+            if (key > lim) sc[q][t][r] = -INFINITY;
+          }
+      }
     }
 
-    // block row max (in-lane, then across the two half-waves)
-    const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
-    // lazy rescale: only when some row's max grew by more than 2^kLazy
-    // (m_run = -inf and a finite m_new gives +inf > kLazy; both -inf give NaN)
-    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy)) {
-      // 0 when m_run = -inf < m_new; rows whose max is still -inf hold O = 0
-      // and l = 0 and keep them (their alpha would be exp2(NaN))
-      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
-      m_run = m_new;
-      l_run *= alpha;
+    // block row max (in-lane, then across the two half-waves); lazy rescale
+    // only when some row's max grew by more than 2^kLazy (m_run = -inf and a
+    // finite m_new gives +inf > kLazy; both -inf give NaN)
+    float m_new[QG];
+    bool grow = false;
 #pragma unroll
-      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+    for (int q = 0; q < QG; ++q) {
+      m_new[q] = fmax_nan(m_run[q], halfwave_max(block_max(sc[q])));
+      grow = grow || (m_new[q] - m_run[q]) * c > kLazy;
     }
-    const float ms = (m_run == -INFINITY ? 0.f : m_run) * c;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+      // With QG = 2 the O accumulators live in AGPRs and the scaling below
+      // needs VGPR copies; redefining them here keeps the compiler from
+      // hoisting those copies out of this rarely taken branch.
+      if constexpr (QG == 2) {
+#pragma unroll
+        for (int q = 0; q < QG; ++q) pin_accumulators_agpr(oacc[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < QG; ++q) {
+        // 0 when m_run = -inf < m_new; rows whose max is still -inf hold O = 0
+        // and l = 0 and keep them (their alpha would be exp2(NaN))
+        const float alpha = m_new[q] == -INFINITY ? 1.f : exp2_fast((m_run[q] - m_new[q]) * c);
+        m_run[q] = m_new[q];
+        l_run[q] *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) oacc[q][t] *= alpha;
+      }
+    }
+    float ms[QG];
+#pragma unroll
+    for (int q = 0; q < QG; ++q) ms[q] = (m_run[q] == -INFINITY ? 0.f : m_run[q]) * c;
 
     // P = exp2(c*S - c*m), row sum, bf16 B operands -- interleaved with the
     // MFMAs of the next block's scores
-    float rs = 0.f;
-    bf16x8 pb[4];
+    float rs[QG];
+    bf16x8 pb[QG][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) sn[t] = f32x16{};
+    for (int q = 0; q < QG; ++q) {
+      rs[q] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sn[q][t] = f32x16{};
+    }
 #pragma unroll
     for (int step = 0; step < 16; ++step) {
       const int kc = step >> 1, t = step & 1;
       if (kc < KC) {
         bf16x8 a = *(const bf16x8*)(kread + 32 * t * RB + ka[kc]);
-        sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], sn[t], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < QG; ++q)
+          sn[q][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[q][kc], sn[q][t], 0, 0, 0);
       }
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {  // two of this lane's 32 scores per step
-        const int idx = 2 * step + e;
-        const int tt = idx >> 4, r = idx & 15;
-        const float pv = exp2_fast(__builtin_fmaf(sc[tt][r], c, -ms));
-        rs += pv;
-        pb[2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
-      }
+      for (int q = 0; q < QG; ++q)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {  // two of this lane's 32 scores per step and group
+          const int idx = 2 * step + e;
+          const int tt = idx >> 4, r = idx & 15;
+          const float pv = exp2_fast(__builtin_fmaf(sc[q][tt][r], c, -ms[q]));
+          rs[q] += pv;
+          pb[q][2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
+        }
     }
-    l_run += rs;
+#pragma unroll
+    for (int q = 0; q < QG; ++q) l_run[q] += rs[q];
 
     // O^T += V_n^T P^T
 #pragma unroll
@@ -402,7 +477,9 @@ void fa_fwd_bf16_kernel(Params p) {
             (__attribute__((address_space(3))) i16x4*)(vread + (16 * kc2 + 4) * RB + va[t]));
         bf16x4 lob = __builtin_bit_cast(bf16x4, lo), hib = __builtin_bit_cast(bf16x4, hi);
         bf16x8 a = {lob[0], lob[1], lob[2], lob[3], hib[0], hib[1], hib[2], hib[3]};
-        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], oacc[t], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < QG; ++q)
+          oacc[q][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[q][kc2], oacc[q][t], 0, 0, 0);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -413,27 +490,52 @@ void fa_fwd_bf16_kernel(Params p) {
   char* const k1b = kbuf0 + BUF;
   char* const v0b = vbuf0;
   char* const v1b = vbuf0 + BUF;
-  for (int it = 0; it < nblk; it += 2) {
-    iteration(it, s_a, s_b, k1b, v0b, k0b, v1b);
+  // Blocks are consumed from the last to the first, so the ones that need a
+  // mask (past the end of the keys, or crossing the causal diagonal) come
+  // first: block n needs one iff (n + 1) * TN > thr.  The masked iterations
+  // (rounded up to an even count, so the unmasked loop starts on buffer 0)
+  // run in a loop of their own; the main loop carries no mask code.
+  const int thr = CAUSAL ? min(si.sk, m0 + diag + 1) : si.sk;
+  const int n_plain = thr <= 0 ? 0 : min(nblk, thr / TN);  // blocks 0 .. n_plain-1 need no mask
+  const int it_mask_end = min(nblk, (nblk - n_plain + 1) & ~1);
+  int it = 0;
+  for (; it < it_mask_end; it += 2) {
+    iteration(it, s_a, s_b, k1b, v0b, k0b, v1b, BoolTag<true>{});
+    if (it + 1 == nblk) {
+      it = nblk;
+      break;
+    }
+    iteration(it + 1, s_b, s_a, k0b, v1b, k1b, v0b, BoolTag<true>{});
+  }
+  for (; it < nblk; it += 2) {
+    iteration(it, s_a, s_b, k1b, v0b, k0b, v1b, BoolTag<false>{});
     if (it + 1 == nblk) break;
-    iteration(it + 1, s_b, s_a, k0b, v1b, k1b, v0b);
+    iteration(it + 1, s_b, s_a, k0b, v1b, k1b, v0b, BoolTag<false>{});
   }
 
   // ---- epilogue: normalise, O (bf16) and LSE (natural log)
-  pin_accumulators(oacc);
-  const float l_tot = halfwave_sum(l_run);
-  if (!qvalid) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-  for (int t = 0; t < DT; ++t)
+  for (int q = 0; q < QG; ++q) {
+    if constexpr (QG == 1) pin_accumulators(oacc[q]);
+    else pin_accumulators_agpr(oacc[q]);
+  }
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      bf16x4 ov;
+  for (int q = 0; q < QG; ++q) {
+    const float l_tot = halfwave_sum(l_run[q]);
+    if (!qvalid[q]) continue;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(oacc[t][4 * i4 + j] * inv);
-      *(bf16x4*)(O + orow + 32 * t + 8 * i4 + 4 * hf) = ov;
-    }
-  if (hf == 0) p.lse[lse_idx] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 ov;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(oacc[q][t][4 * i4 + j] * inv);
+        *(bf16x4*)(O + orow[q] + 32 * t + 8 * i4 + 4 * hf) = ov;
+      }
+    if (hf == 0)
+      p.lse[lse_idx[q]] = l_tot > 0.f ? (m_run[q] * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -733,8 +835,12 @@ void launch_fp8(const Launch& L, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 void launch_bf16(const Launch& L, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)L.num_workgroups), dim3(256), 0,
-                     stream, L.p);
+  if (L.query_tiles == 2)
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, 2>), dim3((unsigned)L.num_workgroups),
+                       dim3(256), 0, stream, L.p);
+  else
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, 1>), dim3((unsigned)L.num_workgroups),
+                       dim3(256), 0, stream, L.p);
 }
 
 int device_is_gfx950() {

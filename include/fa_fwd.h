@@ -157,10 +157,29 @@ typedef struct fa_plan {
  * fa_fwd_plan -- choose the kernel configuration for a shape (pure host
  * function, no HIP call).  dev == NULL means gfx950.  Returns FA_OK,
  * FA_ERR_NULL, FA_ERR_INVALID or FA_ERR_UNSUPPORTED (nothing fits `dev`).
+ *
+ * The plan uses query_tiles = 1 (128 query rows per workgroup, two waves per
+ * SIMD) unless fa_set_query_tiles forces 2 for bf16 (256 rows per workgroup,
+ * one wave per SIMD holding the full register file, every LDS operand read
+ * feeding two matrix instructions).  fp8 always uses 1.
  */
 int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
                 int varlen, int head_dim, int head_dim_v, int causal,
                 const fa_device_limits_t* dev, fa_plan_t* out);
+
+/*
+ * fa_set_query_tiles -- tuning override of the planner's tiling choice for
+ * bf16 (for benchmarking and for tests that exercise both tilings on the
+ * same shapes).  0 restores the automatic choice; 1 or 2 forces that many
+ * 32-row query tiles per wave in every later fa_fwd / fa_fwd_plan call of the
+ * process (fp8 always uses 1).  Both tilings compute the same function to
+ * within rounding, but not bit for bit: the reference maximum that the
+ * softmax rescales against is updated per wave, and a wave holds different
+ * rows in the two tilings.  The setting is a process-wide atomic; calls
+ * already launched are unaffected.  Returns FA_OK, or FA_ERR_INVALID for any
+ * other value.
+ */
+int fa_set_query_tiles(int query_tiles);
 
 /* Library version: major*10000 + minor*100 + patch. */
 int fa_version(void);

@@ -11,6 +11,16 @@ from parity import compare, gather_rows, gpu_run, oracle_full, oracle_rows, samp
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=[1, 2], ids=["qt1", "qt2"])
+def query_tiles(request):
+    """Force each bf16 tiling (1 or 2 query tiles of 32 rows per wave) for the test."""
+    import exact_attention_forward_fa_amd as fa
+
+    fa.fa_set_query_tiles(request.param)
+    yield request.param
+    fa.fa_set_query_tiles(0)
+
+
 def full_check(w):
     o, lse = gpu_run(w)
     ro, rl = oracle_full(w)
@@ -35,13 +45,26 @@ def test_tiny_noncausal_d64():
 
 
 @pytest.mark.parametrize("name", ["mha_b4_h16_s1024_d128", "mha_causal_b4_h16_s1024_d128"])
-def test_mha_1024(name):
+def test_mha_1024(name, query_tiles):
     full_check(fa_inputs.workload(name))
 
 
 def test_gqa_causal_8192_sampled():
     w = fa_inputs.workload("gqa_causal_b2_hq32_hkv8_s8192_d128")
     o, lse = sampled_check(w, n_random=32)
+    assert np.isfinite(lse).all() and np.isfinite(o).all()
+
+
+def test_gqa_causal_8192_sampled_one_tile_per_wave():
+    """The same workload through the 128-row tiling (the planner picks 256 rows for it)."""
+    import exact_attention_forward_fa_amd as fa
+
+    w = fa_inputs.workload("gqa_causal_b2_hq32_hkv8_s8192_d128")
+    fa.fa_set_query_tiles(1)
+    try:
+        o, lse = sampled_check(w, n_random=16)
+    finally:
+        fa.fa_set_query_tiles(0)
     assert np.isfinite(lse).all() and np.isfinite(o).all()
 
 
@@ -58,8 +81,8 @@ def test_varlen_causal_sampled():
         assert np.all(np.isfinite(lse[:, q0 + dead:q0 + sq]))
 
 
-def test_varlen_equals_per_sequence_calls():
-    """Packed varlen output equals separate fixed-length calls, bit for bit."""
+def test_varlen_equals_per_sequence_calls(query_tiles):
+    """Packed varlen output equals separate fixed-length calls, bit for bit (same tiling)."""
     lens = [(300, 517), (1, 64), (129, 100), (64, 0), (0, 40), (255, 256), (70, 700)]
     w = fa_inputs.make(0, 4, 2, 0, 0, 128, causal=True, seed=50, lengths=lens, name="varlen_small")
     o, lse = gpu_run(w)
@@ -87,10 +110,10 @@ def test_varlen_equals_per_sequence_calls():
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 4, 4, 300, 300), (1, 8, 2, 200, 517), (1, 4, 1, 517, 200),
                                    (3, 2, 2, 1, 1), (1, 2, 2, 1, 333), (1, 32, 1, 130, 130)])
-def test_ragged_shapes(shape, causal, d):
+def test_ragged_shapes(shape, causal, d, query_tiles):
     b, hq, hkv, sq, sk = shape
     w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq * 7 + sk + d,
-                       name=f"ragged_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}_c{int(causal)}")
+                       name=f"ragged_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}_c{int(causal)}_qt{query_tiles}")
     full_check(w)
 
 
@@ -100,12 +123,12 @@ def test_seqlen_k_zero():
     assert np.all(o == 0.0) and np.all(lse == -np.inf)
 
 
-def test_large_q_magnitude():
+def test_large_q_magnitude(query_tiles):
     w = fa_inputs.make(1, 4, 4, 256, 256, 128, causal=True, seed=61, q_mult=50.0, name="q_x50")
     full_check(w)
 
 
-def test_gqa_equals_repeated_mha_on_gpu():
+def test_gqa_equals_repeated_mha_on_gpu(query_tiles):
     w = fa_inputs.make(1, 8, 2, 257, 257, 128, causal=True, seed=62, name="gqa")
     o1, l1 = gpu_run(w)
     w2 = fa_inputs.make(1, 8, 2, 257, 257, 128, causal=True, seed=62, name="gqa_as_mha")
@@ -116,7 +139,7 @@ def test_gqa_equals_repeated_mha_on_gpu():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_deterministic():
+def test_deterministic(query_tiles):
     w = fa_inputs.make(2, 8, 2, 700, 700, 128, causal=True, seed=63, name="det")
     t = to_device(w)
     o1, l1 = gpu_run(w, t)
@@ -124,7 +147,7 @@ def test_deterministic():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_no_writes_outside_outputs():
+def test_no_writes_outside_outputs(query_tiles):
     """Outputs carved from larger buffers filled with a sentinel: nothing past the ends changes."""
     import exact_attention_forward_fa_amd as fa
 
