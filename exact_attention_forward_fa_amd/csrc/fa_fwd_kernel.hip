@@ -735,15 +735,15 @@ void fa_fwd_fp8_kernel(Params p) {
 
   auto iteration = [&](const int it, f32x16 (&sc)[2], f32x16 (&sn)[2],
                        const char* __restrict__ kread, const char* __restrict__ vread,
-                       char* __restrict__ kdst, char* __restrict__ vdst) __attribute__((always_inline)) {
+                       char* __restrict__ kdst, char* __restrict__ vdst,
+                       auto mask_tag) __attribute__((always_inline)) {
     const int n = nblk - 1 - it;
     __syncthreads();
     if (n >= 2) stage(kseq, koff, kdst, n - 2);
     if (n >= 1) stage(vseq, voff, vdst, n - 1);
 
     // mask: key of register r of sub-tile t in half hf is n*TN + 32hf + 16t + r
-    const bool need_mask = (n + 1) * TN > si.sk || (CAUSAL && (n + 1) * TN - 1 > m0 + diag);
-    if (need_mask) {
+    if (decltype(mask_tag)::value) {
       const int lim = CAUSAL ? min(si.sk - 1, qi + diag) : si.sk - 1;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -753,7 +753,7 @@ void fa_fwd_fp8_kernel(Params p) {
     }
 
     const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
-    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy) != 0, 0)) {
       const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
       m_run = m_new;
       l_run *= alpha;
@@ -805,10 +805,23 @@ void fa_fwd_fp8_kernel(Params p) {
   char* const k1b = kbuf0 + BUF;
   char* const v0b = vbuf0;
   char* const v1b = vbuf0 + BUF;
-  for (int it = 0; it < nblk; it += 2) {
-    iteration(it, s_a, s_b, k1b, v0b, k0b, v1b);
+  // masked iterations first, in a loop of their own (as in the bf16 kernel)
+  const int thr = CAUSAL ? min(si.sk, m0 + diag + 1) : si.sk;
+  const int n_plain = thr <= 0 ? 0 : min(nblk, thr / TN);  // blocks 0 .. n_plain-1 need no mask
+  const int it_mask_end = min(nblk, (nblk - n_plain + 1) & ~1);
+  int it = 0;
+  for (; it < it_mask_end; it += 2) {
+    iteration(it, s_a, s_b, k1b, v0b, k0b, v1b, BoolTag<true>{});
+    if (it + 1 == nblk) {
+      it = nblk;
+      break;
+    }
+    iteration(it + 1, s_b, s_a, k0b, v1b, k1b, v0b, BoolTag<true>{});
+  }
+  for (; it < nblk; it += 2) {
+    iteration(it, s_a, s_b, k1b, v0b, k0b, v1b, BoolTag<false>{});
     if (it + 1 == nblk) break;
-    iteration(it + 1, s_b, s_a, k0b, v1b, k1b, v0b);
+    iteration(it + 1, s_b, s_a, k0b, v1b, k1b, v0b, BoolTag<false>{});
   }
 
   pin_accumulators(oacc);
