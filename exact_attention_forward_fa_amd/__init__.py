@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     Screen,
     TileConfig,
     fa_fwd,
+    fa_fwd_kvcache,
     fa_fwd_plan,
     fa_set_query_tiles,
     fa_gfx950_limits,
@@ -35,5 +36,6 @@ from ._binding import (  # noqa: F401
     fa_strerror,
     fa_version,
     forward,
+    forward_kvcache,
     library_path,
 )

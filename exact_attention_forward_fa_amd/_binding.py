@@ -83,6 +83,9 @@ def _load():
     lib.fa_version.restype = i32
     lib.fa_set_query_tiles.argtypes = [i32]
     lib.fa_set_query_tiles.restype = i32
+    lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
+                                   i32, i32, ctypes.c_float, i32, vp, vp]
+    lib.fa_fwd_kvcache.restype = i32
     return lib
 
 
@@ -212,4 +215,58 @@ def forward(q, k, v, *, causal: bool, softmax_scale: Optional[float] = None, cu_
         lse = torch.empty((hq, total_q), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, out, lse, batch, hq, hkv, sq, sk, cu_seqlens, d, dv, softmax_scale,
            int(bool(causal)), descales)
+    return out, lse
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, k_new, v_new, o, lse, batch: int, heads_q: int,
+                   heads_kv: int, seqlen_q: int, seqlen_new: int, cache_capacity: int,
+                   cache_seqlens, head_dim: int, head_dim_v: int, softmax_scale: float, causal,
+                   descales, stream=None) -> int:
+    """Call the C entry point (append new K/V to the cache, then the forward over it)."""
+    st = _current_stream() if stream is None else int(stream)
+    rc = _lib.fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                             _ptr(o), _ptr(lse), int(batch), int(heads_q), int(heads_kv),
+                             int(seqlen_q), int(seqlen_new), int(cache_capacity),
+                             _ptr(cache_seqlens), int(head_dim), int(head_dim_v),
+                             ctypes.c_float(float(softmax_scale)), int(causal), _ptr(descales), st)
+    if rc:
+        raise FaError(rc, "fa_fwd_kvcache")
+    return rc
+
+
+def forward_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, *, causal: bool,
+                    softmax_scale: Optional[float] = None, descales=None, out=None, lse=None):
+    """Append (k_new, v_new) to the caches and attend over them.
+
+    q [B, Sq, Hq, D]; k_cache / v_cache [B, capacity, Hkv, D] (updated in place); k_new / v_new
+    [B, Snew, Hkv, D] or None; cache_seqlens int32[B] on the GPU (not advanced).  bf16, or e4m3
+    codes with ``descales``.  Returns (O [B*Sq, Hq, D], LSE [Hq, B*Sq]).
+    """
+    import torch
+
+    tensors = [("q", q), ("k_cache", k_cache), ("v_cache", v_cache)]
+    if k_new is not None or v_new is not None:
+        if k_new is None or v_new is None:
+            raise ValueError("k_new and v_new go together")
+        tensors += [("k_new", k_new), ("v_new", v_new)]
+    fp8 = descales is not None
+    want = (torch.uint8, torch.float8_e4m3fn) if fp8 else (torch.bfloat16,)
+    for name, t in tensors:
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d GPU tensor")
+        if t.dtype not in want:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected one of {want}")
+    b, sq, hq, d = q.shape
+    _, cap, hkv, _ = k_cache.shape
+    snew = 0 if k_new is None else k_new.shape[1]
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda or cache_seqlens.numel() != b:
+        raise ValueError("cache_seqlens must be int32[batch] on the GPU")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((b * sq, hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, b * sq), dtype=torch.float32, device=q.device)
+    fa_fwd_kvcache(q, k_cache, v_cache, k_new, v_new, out, lse, b, hq, hkv, sq, snew, cap,
+                   cache_seqlens, d, d, softmax_scale, int(bool(causal)), descales)
     return out, lse

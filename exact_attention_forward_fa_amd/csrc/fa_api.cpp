@@ -132,10 +132,17 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   return FA_OK;
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
-           int heads_q, int heads_kv, int seqlen_q, int seqlen_k, const int* cu_seqlens,
-           int head_dim, int head_dim_v, float softmax_scale, int causal, const float* descales,
-           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward launch shared by fa_fwd and fa_fwd_kvcache.  cache_seqlens ==
+// NULL: K/V rows per sequence as fa_fwd documents; else the KV-cache mode
+// (fixed-length layout with seqlen_k = cache capacity, cu_seqlens NULL).
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                 int heads_q, int heads_kv, int seqlen_q, int seqlen_k, const int* cu_seqlens,
+                 const int* cache_seqlens, int seqlen_new, int head_dim, int head_dim_v,
+                 float softmax_scale, int causal, const float* descales, void* stream) {
   int rc = check_dims(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, head_dim_v);
   if (rc) return rc;
   // Q/O/LSE may be NULL only when there is provably no query row, K/V only
@@ -155,6 +162,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   // whose byte range is a 31-bit quantity.
   const int64_t elem = dtype == FA_DTYPE_E4M3 ? 1 : 2;
   if ((int64_t)seqlen_k * heads_kv * head_dim * elem >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  // sequence offsets (rows) are 32-bit in the kernel
+  if (!cu_seqlens && ((int64_t)batch * seqlen_q >= (1LL << 31) ||
+                      (int64_t)batch * seqlen_k >= (1LL << 31)))
+    return FA_ERR_UNSUPPORTED;
   if (plan.num_workgroups == 0) return FA_OK;  // no query rows: nothing to write
   fa::Launch L;
   L.p.q = q;
@@ -164,6 +175,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   L.p.lse = lse;
   L.p.cu = cu_seqlens;
   L.p.descales = descales;
+  L.p.cache_seqlens = cache_seqlens;
+  L.p.seqlen_new = seqlen_new;
   L.p.batch = batch;
   L.p.hq = heads_q;
   L.p.hkv = heads_kv;
@@ -178,6 +191,56 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   L.num_workgroups = plan.num_workgroups;
   L.query_tiles = qt;
   return fa::launch(L, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+           int heads_q, int heads_kv, int seqlen_q, int seqlen_k, const int* cu_seqlens,
+           int head_dim, int head_dim_v, float softmax_scale, int causal, const float* descales,
+           void* stream) {
+  return forward_impl(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k, cu_seqlens,
+                      nullptr, 0, head_dim, head_dim_v, softmax_scale, causal, descales, stream);
+}
+
+int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const void* k_new,
+                   const void* v_new, void* o, float* lse, int batch, int heads_q, int heads_kv,
+                   int seqlen_q, int seqlen_new, int cache_capacity, const int* cache_seqlens,
+                   int head_dim, int head_dim_v, float softmax_scale, int causal,
+                   const float* descales, void* stream) {
+  if (seqlen_new < 0 || cache_capacity < 0) return FA_ERR_INVALID;
+  int rc = check_dims(batch, heads_q, heads_kv, seqlen_q, cache_capacity, head_dim, head_dim_v);
+  if (rc) return rc;
+  if (!cache_seqlens) return FA_ERR_NULL;
+  if ((!k_new || !v_new) && seqlen_new > 0) return FA_ERR_NULL;
+  if ((!k_cache || !v_cache) && cache_capacity > 0) return FA_ERR_NULL;
+  if ((head_dim != 64 && head_dim != 128) || head_dim_v != head_dim) return FA_ERR_UNSUPPORTED;
+  const int64_t elem = descales ? 1 : 2;
+  if ((int64_t)cache_capacity * heads_kv * head_dim * elem >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * seqlen_new * heads_kv * head_dim * elem >= (1LL << 40)) return FA_ERR_UNSUPPORTED;
+  // validate the forward's own arguments before anything is written
+  if ((!q || !o || !lse) && seqlen_q > 0) return FA_ERR_NULL;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (seqlen_new > 0 && cache_capacity > 0) {
+    fa::Append A;
+    A.k_cache = k_cache;
+    A.v_cache = v_cache;
+    A.k_new = k_new;
+    A.v_new = v_new;
+    A.cache_seqlens = cache_seqlens;
+    A.batch = batch;
+    A.seqlen_new = seqlen_new;
+    A.capacity = cache_capacity;
+    A.row_bytes = (int)(heads_kv * head_dim * elem);
+    rc = fa::launch_append(A, stream);
+    if (rc) return rc;
+  }
+  return forward_impl(q, k_cache, v_cache, o, lse, batch, heads_q, heads_kv, seqlen_q,
+                      cache_capacity, nullptr, cache_seqlens, seqlen_new, head_dim, head_dim_v,
+                      softmax_scale, causal, descales, stream);
 }
 
 }  // extern "C"

@@ -100,6 +100,7 @@ __device__ __forceinline__ SeqInfo seq_info(const Params& p, int b) {
     s.k0 = b * p.seqlen_k;
     s.sk = p.seqlen_k;
     s.total_q = p.batch * p.seqlen_q;
+    if (p.cache_seqlens) s.sk = max(0, min(p.cache_seqlens[b] + p.seqlen_new, p.seqlen_k));
   }
   return s;
 }
@@ -856,6 +857,28 @@ void launch_bf16(const Launch& L, hipStream_t stream) {
                        dim3(256), 0, stream, L.p);
 }
 
+// AppendKV: copy the new K and V rows into the caches.  One thread moves 16
+// bytes; thread i of the grid handles byte 16*(i % chunks) of new row
+// i / chunks (rows ordered [b][j], K rows then V rows).
+__global__ __launch_bounds__(256) void append_kv_kernel(Append a) {
+  const int chunks = a.row_bytes / 16;
+  const int64_t rows = (int64_t)a.batch * a.seqlen_new;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * rows * chunks) return;
+  const int64_t r = i / chunks;
+  const int ch = (int)(i - r * chunks);
+  const bool is_v = r >= rows;
+  const int64_t rr = is_v ? r - rows : r;
+  const int b = (int)(rr / a.seqlen_new);
+  const int j = (int)(rr - (int64_t)b * a.seqlen_new);
+  const int pos = a.cache_seqlens[b] + j;
+  if (pos < 0 || pos >= a.capacity) return;
+  const char* src = (const char*)(is_v ? a.v_new : a.k_new) + rr * a.row_bytes + 16 * ch;
+  char* dst = (char*)(is_v ? a.v_cache : a.k_cache) +
+              ((int64_t)b * a.capacity + pos) * a.row_bytes + 16 * ch;
+  *(u32x4*)dst = *(const u32x4*)src;
+}
+
 int device_is_gfx950() {
   static int cached[64];  // 0 unknown, 1 yes, -1 no
   int dev = 0;
@@ -871,6 +894,16 @@ int device_is_gfx950() {
 }
 
 }  // namespace
+
+int launch_append(const Append& A, void* stream_) {
+  if (!device_is_gfx950()) return FA_ERR_DEVICE;
+  const int64_t threads = 2 * (int64_t)A.batch * A.seqlen_new * (A.row_bytes / 16);
+  if (threads == 0) return FA_OK;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream_, A);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_DEVICE;
+}
 
 int launch(const Launch& L, void* stream_) {
   if (!device_is_gfx950()) return FA_ERR_DEVICE;

@@ -27,6 +27,11 @@ struct Params {
   float* lse;
   const int* cu;          // NULL or int32[2*(batch+1)]
   const float* descales;  // NULL or float[3]
+  // KV-cache mode (cu == NULL): sequence b's keys are rows b*seqlen_k ..
+  // of K/V (seqlen_k = cache capacity), of which the first
+  // min(cache_seqlens[b] + seqlen_new, seqlen_k) are used
+  const int* cache_seqlens;
+  int seqlen_new;
   int batch, hq, hkv, group, seqlen_q, seqlen_k;
   int m_tiles;            // query tiles per (sequence, head)
   float scale_log2;       // softmax_scale * log2(e)
@@ -43,5 +48,21 @@ struct Launch {
 
 // Returns 0, or FA_ERR_DEVICE when the device is not gfx950 or the launch fails.
 int launch(const Launch& L, void* stream);
+
+// Appending new K/V rows to a KV cache: rows [b][j] (j < seqlen_new) of
+// k_new / v_new go to rows [b][cache_seqlens[b] + j] of the caches; rows
+// whose position falls outside [0, capacity) are skipped.
+struct Append {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;
+  const void* v_new;
+  const int* cache_seqlens;
+  int batch, seqlen_new, capacity;
+  int row_bytes;  // heads_kv * head_dim * element bytes (a multiple of 16)
+};
+
+// Same return convention as launch().
+int launch_append(const Append& A, void* stream);
 
 }  // namespace fa

@@ -15,8 +15,12 @@ Recipe (every workload):
   * variable-length batches draw their lengths from
     ``numpy.random.default_rng(seed)`` and pack sequences back to back;
     ``cu_seqlens`` is int32[2*(batch+1)]: query offsets, then key offsets.
+  * KV-cache cases draw q, k_cache, v_cache, k_new, v_new in that order; the
+    whole cache is filled (rows past the used length too); fp8 quantises the
+    cache and the new rows of K (and of V) with one shared descale.
 
-Layouts: Q [total_q][Hq][D], K [total_k][Hkv][D], V [total_k][Hkv][Dv].
+Layouts: Q [total_q][Hq][D], K [total_k][Hkv][D], V [total_k][Hkv][Dv];
+KV cache [B][capacity][Hkv][D], new rows [B][Snew][Hkv][D].
 """
 from __future__ import annotations
 
@@ -118,6 +122,61 @@ def make(batch: int, heads_q: int, heads_kv: int, seqlen_q: int, seqlen_k: int, 
                     seqlen_k=seqlen_k, head_dim=head_dim, head_dim_v=dv, softmax_scale=scale,
                     causal=causal, dtype=dtype, q=q, k=k, v=v, cu_seqlens=cu, descales=descales,
                     seed=seed, lengths=lens)
+
+
+@dataclass
+class KVCacheCase:
+    """Inputs of one KV-cache forward: q [B, Sq, Hq, D], caches [B, cap, Hkv, D], new rows
+    [B, Snew, Hkv, D] (None when Snew = 0), cache_seqlens int32[B]; raw codes (bf16, or e4m3
+    uint8 with descales float32[3] shared by the cache and the new rows)."""
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    k_new: Optional[torch.Tensor]
+    v_new: Optional[torch.Tensor]
+    cache_seqlens: np.ndarray
+    softmax_scale: float
+    causal: bool
+    dtype: str
+    descales: Optional[np.ndarray] = None
+
+
+def make_kvcache(batch: int, seqlen_q: int, seqlen_new: int, capacity: int, cache_seqlens,
+                 heads_q: int, heads_kv: int, head_dim: int, *, causal: bool, seed: int,
+                 dtype: str = "bf16", fp8_mult: float = 0.5) -> KVCacheCase:
+    """Seeded KV-cache inputs, drawn in the order q, k_cache, v_cache, k_new, v_new.  The whole
+    cache is filled with data (rows past cache_seqlens too), so a kernel that reads beyond
+    the used length gives a wrong answer instead of a lucky zero.  fp8: one descale per
+    tensor family, taken over the cache and the new rows together (a cache has one scale)."""
+    g = torch.Generator().manual_seed(seed)
+    scale = 1.0 / math.sqrt(head_dim)
+    shp_q = (batch, seqlen_q, heads_q, head_dim)
+    shp_c = (batch, capacity, heads_kv, head_dim)
+    shp_n = (batch, seqlen_new, heads_kv, head_dim)
+    lens = np.asarray(cache_seqlens, dtype=np.int32).reshape(batch)
+    if dtype == "bf16":
+        q = _randn(g, shp_q).to(torch.bfloat16)
+        kc = _randn(g, shp_c).to(torch.bfloat16)
+        vc = _randn(g, shp_c).to(torch.bfloat16)
+        kn = _randn(g, shp_n).to(torch.bfloat16)
+        vn = _randn(g, shp_n).to(torch.bfloat16)
+        descales = None
+    elif dtype == "e4m3":
+        q, dq = _quant_e4m3(_randn(g, shp_q, fp8_mult))
+        k_all, dk = _quant_e4m3(torch.cat([_randn(g, shp_c, fp8_mult).reshape(-1),
+                                           _randn(g, shp_n, fp8_mult).reshape(-1)]))
+        v_all, dvs = _quant_e4m3(torch.cat([_randn(g, shp_c, fp8_mult).reshape(-1),
+                                            _randn(g, shp_n, fp8_mult).reshape(-1)]))
+        nc = int(np.prod(shp_c))
+        kc, kn = k_all[:nc].reshape(shp_c).contiguous(), k_all[nc:].reshape(shp_n).contiguous()
+        vc, vn = v_all[:nc].reshape(shp_c).contiguous(), v_all[nc:].reshape(shp_n).contiguous()
+        descales = np.array([dq, dk, dvs], dtype=np.float32)
+    else:
+        raise ValueError(dtype)
+    if seqlen_new == 0:
+        kn = vn = None
+    return KVCacheCase(q=q, k_cache=kc, v_cache=vc, k_new=kn, v_new=vn, cache_seqlens=lens,
+                       softmax_scale=scale, causal=causal, dtype=dtype, descales=descales)
 
 
 def varlen_lengths(seed: int = 4, n_long_k: int = 16, n_short_k: int = 2) -> List[Tuple[int, int]]:

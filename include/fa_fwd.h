@@ -98,6 +98,41 @@ const char* fa_strerror(int code);
 /* ---- tile / occupancy screening (pure host functions) ------------------ */
 
 /*
+ * fa_fwd_kvcache -- append new keys/values to a KV cache, then run the
+ * forward pass over the cache: the AppendKV step of "FlashAttention core
+ * algorithm: forward pass" (the producer loop loads the new K/V before the
+ * tile's K/V when AppendKV is enabled), read as the usual cached forward:
+ *
+ *   1. for every sequence b and j < seqlen_new, rows k_new[b][j] and
+ *      v_new[b][j] are copied to k_cache[b][cache_seqlens[b] + j] and
+ *      v_cache[b][cache_seqlens[b] + j] (positions outside
+ *      [0, cache_capacity) are skipped);
+ *   2. fa_fwd over Q [batch][seqlen_q][heads_q][head_dim] (fixed length) and
+ *      the first sk_b = clamp(cache_seqlens[b] + seqlen_new, 0,
+ *      cache_capacity) rows of sequence b's cache, with bottom-right causal
+ *      alignment when causal = 1 (the last query sees the last key).
+ *
+ *   k_cache, v_cache   device, [batch][cache_capacity][heads_kv][head_dim]
+ *                      (bf16, or e4m3 codes when descales != NULL); updated
+ *                      in place
+ *   k_new, v_new       device, [batch][seqlen_new][heads_kv][head_dim]
+ *   cache_seqlens      device int32[batch]: rows already in each cache
+ *                      (read, not updated: the caller advances it)
+ *   q, o, lse, batch, heads, head dims, softmax_scale, causal, descales
+ *                      as for fa_fwd, with total_q = batch * seqlen_q
+ *
+ * The append runs as its own kernel on `stream` before the attention
+ * kernel.  Returns FA_OK or a negative code; argument errors are reported
+ * before anything is launched or written.  k_new / v_new may be NULL when
+ * seqlen_new == 0, the caches when cache_capacity == 0.
+ */
+int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const void* k_new,
+                   const void* v_new, void* o, float* lse, int batch, int heads_q, int heads_kv,
+                   int seqlen_q, int seqlen_new, int cache_capacity, const int* cache_seqlens,
+                   int head_dim, int head_dim_v, float softmax_scale, int causal,
+                   const float* descales, void* stream);
+
+/*
  * Capacity figures of a device, as the shared-memory screen of "FlashAttention
  * on SM120 reusing the SM80 forward" (section on can_implement and the
  * appendix table of per-SM / per-block shared memory) uses them.  On gfx950

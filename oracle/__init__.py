@@ -154,6 +154,56 @@ def probs_row(q, k, v, b, h, i, *, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
     return p, o, float(lse[0])
 
 
+def append_kv(k_cache, v_cache, k_new, v_new, cache_seqlens, *, dtype=BF16):
+    """The append step of the KV-cache forward (the AppendKV branch of the forward-pass page's
+    producer loop, read as the usual cached forward): copies of the caches in which row j of
+    sequence b's new keys/values sits at position cache_seqlens[b] + j; positions outside
+    [0, capacity) are dropped.  Caches [B, cap, Hkv, D], new rows [B, Snew, Hkv, D], as raw
+    codes.  Returns (k_cache', v_cache', lengths) with lengths[b] = clamp(cache_seqlens[b] +
+    Snew, 0, cap), the number of cache rows the attention step reads."""
+    kc = _as_bits(k_cache, dtype).copy()
+    vc = _as_bits(v_cache, dtype).copy()
+    lens = np.asarray(cache_seqlens, dtype=np.int64).reshape(-1)
+    cap = kc.shape[1]
+    if k_new is not None:
+        kn = _as_bits(k_new, dtype)
+        vn = _as_bits(v_new, dtype)
+        for b in range(kc.shape[0]):
+            for j in range(kn.shape[1]):
+                pos = int(lens[b]) + j
+                if 0 <= pos < cap:
+                    kc[b, pos] = kn[b, j]
+                    vc[b, pos] = vn[b, j]
+        snew = kn.shape[1]
+    else:
+        snew = 0
+    used = np.clip(lens + snew, 0, cap)
+    return kc, vc, used
+
+
+def attention_kvcache(q, k_cache, v_cache, k_new, v_new, cache_seqlens, *, softmax_scale, causal,
+                      descales=None, dtype=BF16):
+    """KV-cache forward: append_kv, then the plain forward of sequence b's queries
+    (q [B, Sq, Hq, D]) over the first lengths[b] rows of its cache, bottom-right causal.
+    Returns (O [B*Sq, Hq, D], LSE [Hq, B*Sq], k_cache', v_cache') with O, LSE float64."""
+    qb = _as_bits(q, dtype)
+    kc, vc, used = append_kv(k_cache, v_cache, k_new, v_new, cache_seqlens, dtype=dtype)
+    b, sq, hq, d = qb.shape
+    hkv = kc.shape[2]
+    # pack the used cache rows as a variable-length batch: [q offsets][k offsets]
+    k_off = np.concatenate([[0], np.cumsum(used)]).astype(np.int32)
+    q_off = (np.arange(b + 1) * sq).astype(np.int32)
+    kp = np.concatenate([kc[i, :used[i]] for i in range(b)], axis=0) if used.sum() else \
+        np.zeros((0, hkv, d), dtype=kc.dtype)
+    vp = np.concatenate([vc[i, :used[i]] for i in range(b)], axis=0) if used.sum() else \
+        np.zeros((0, hkv, d), dtype=vc.dtype)
+    o, lse = attention(qb.reshape(b * sq, hq, d), kp, vp, batch=b, heads_q=hq, heads_kv=hkv,
+                       seqlen_q=sq, seqlen_k=int(used.max()) if b else 0, head_dim=d,
+                       head_dim_v=d, softmax_scale=softmax_scale, causal=causal,
+                       cu_seqlens=np.concatenate([q_off, k_off]), descales=descales, dtype=dtype)
+    return o, lse, kc, vc
+
+
 def decode_bf16(bits):
     bits = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
     out = np.empty(bits.shape, dtype=np.float64)

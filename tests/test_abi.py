@@ -148,6 +148,40 @@ def test_screen_gfx950_answers():
     assert fa.fa_smem_screen(_block_cfg(161), g).fits == 0
 
 
+def call_kv(**kw):
+    args = dict(q=P, k_cache=P, v_cache=P, k_new=P, v_new=P, o=P, lse=P, batch=2, heads_q=4,
+                heads_kv=2, seqlen_q=16, seqlen_new=4, cache_capacity=64, cache_seqlens=P,
+                head_dim=128, head_dim_v=128, softmax_scale=0.1, causal=1, descales=None, stream=0)
+    args.update(kw)
+    try:
+        return fa.fa_fwd_kvcache(**args)
+    except fa.FaError as e:
+        return e.code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cache_seqlens=None), fa.FA_ERR_NULL),
+    (dict(k_new=None), fa.FA_ERR_NULL),
+    (dict(v_new=None), fa.FA_ERR_NULL),
+    (dict(k_cache=None), fa.FA_ERR_NULL),
+    (dict(v_cache=None), fa.FA_ERR_NULL),
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(o=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(seqlen_new=-1), fa.FA_ERR_INVALID),
+    (dict(cache_capacity=-1), fa.FA_ERR_INVALID),
+    (dict(batch=0), fa.FA_ERR_INVALID),
+    (dict(heads_q=6, heads_kv=4), fa.FA_ERR_INVALID),
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID),
+    (dict(causal=2), fa.FA_ERR_INVALID),
+    (dict(head_dim=96, head_dim_v=96), fa.FA_ERR_UNSUPPORTED),
+    # one sequence's cache must fit the 31-bit byte range of a buffer resource
+    (dict(cache_capacity=(1 << 31) // (2 * 128 * 2)), fa.FA_ERR_UNSUPPORTED),
+])
+def test_kvcache_validation_before_any_hip_call(kw, code):
+    assert call_kv(**kw) == code
+
+
 def test_screen_rejects_bad_sizes():
     cfg = fa.TileConfig(tile_m=0, tile_n=64, head_dim=128, head_dim_v=128, elem_bytes=2,
                         kv_stages=1, q_in_regs=0)

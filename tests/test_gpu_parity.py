@@ -193,3 +193,90 @@ def test_fp8_varlen():
     w = fa_inputs.make(0, 4, 2, 0, 0, 128, causal=True, seed=70, lengths=lens, dtype="e4m3",
                        name="fp8_varlen_small")
     full_check(w)
+
+
+# ------------------------------------------------------- KV cache (AppendKV)
+
+def kvcache_check(case, name):
+    """fa_fwd_kvcache against the oracle: the caches afterwards bit for bit, O/LSE to the
+    tolerance of the input type."""
+    import oracle
+
+    import exact_attention_forward_fa_amd as fa
+
+    def dev(t):
+        return None if t is None else t.cuda()
+
+    q, kc, vc, kn, vn = (dev(case.q), dev(case.k_cache), dev(case.v_cache), dev(case.k_new),
+                         dev(case.v_new))
+    lens = torch.from_numpy(case.cache_seqlens).cuda()
+    ds = None if case.descales is None else torch.from_numpy(case.descales).cuda()
+    say(f"[gpu] fa_fwd_kvcache {name}")
+    o, lse = fa.forward_kvcache(q, kc, vc, lens, kn, vn, causal=case.causal,
+                                softmax_scale=case.softmax_scale, descales=ds)
+    torch.cuda.synchronize()
+    dt = oracle.BF16 if case.dtype == "bf16" else oracle.E4M3
+    ro, rl, rk, rv = oracle.attention_kvcache(case.q, case.k_cache, case.v_cache, case.k_new,
+                                              case.v_new, case.cache_seqlens,
+                                              softmax_scale=case.softmax_scale, causal=case.causal,
+                                              descales=case.descales, dtype=dt)
+
+    def bits(t):
+        t = t.cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if case.dtype == "bf16" else t.numpy()
+
+    assert np.array_equal(bits(kc), rk), f"{name}: K cache after the append"
+    assert np.array_equal(bits(vc), rv), f"{name}: V cache after the append"
+    compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, case.dtype, name)
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kvcache_decode_gqa(causal, query_tiles):
+    """One new token per sequence, cache lengths from empty to exactly full."""
+    case = fa_inputs.make_kvcache(4, 1, 1, 4096, [0, 1000, 4095, 2047], 8, 2, 128, causal=causal,
+                                  seed=80)
+    kvcache_check(case, f"kv_decode_c{int(causal)}_qt{query_tiles}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_kvcache_prefill_chunk(causal, d, query_tiles):
+    """A 300-row chunk appended behind a prefix; the second sequence overflows the cache, so
+    its last new rows are dropped and its length clamps to the capacity."""
+    case = fa_inputs.make_kvcache(2, 300, 300, 2048, [100, 1900], 4, 4, d, causal=causal,
+                                  seed=81 + d)
+    kvcache_check(case, f"kv_chunk_d{d}_c{int(causal)}_qt{query_tiles}")
+
+
+def test_kvcache_no_new_rows():
+    case = fa_inputs.make_kvcache(3, 17, 0, 512, [0, 200, 512], 4, 1, 128, causal=True, seed=84)
+    kvcache_check(case, "kv_no_new_rows")
+
+
+def test_kvcache_equals_packed_varlen_call():
+    """The cached forward reads exactly the appended prefix: same answer as fa_fwd on the
+    packed (prefix + new) sequences, bit for bit."""
+    import exact_attention_forward_fa_amd as fa
+
+    case = fa_inputs.make_kvcache(3, 64, 64, 1024, [10, 500, 960], 8, 2, 128, causal=True, seed=85)
+    o, lse = kvcache_check(case, "kv_vs_varlen")
+    used = [min(int(n) + 64, 1024) for n in case.cache_seqlens]
+    import oracle
+
+    kc, vc, _ = oracle.append_kv(case.k_cache, case.v_cache, case.k_new, case.v_new,
+                                 case.cache_seqlens)
+    kp = torch.from_numpy(np.concatenate([kc[b, :used[b]] for b in range(3)])).view(torch.bfloat16)
+    vp = torch.from_numpy(np.concatenate([vc[b, :used[b]] for b in range(3)])).view(torch.bfloat16)
+    cu = np.concatenate([np.arange(4) * 64, np.concatenate([[0], np.cumsum(used)])]).astype(np.int32)
+    o2, l2 = fa.forward(case.q.reshape(3 * 64, 8, 128).cuda(), kp.cuda(), vp.cuda(), causal=True,
+                        softmax_scale=case.softmax_scale, cu_seqlens=torch.from_numpy(cu).cuda(),
+                        max_seqlen_q=64, max_seqlen_k=max(used))
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu(), o2.cpu()) and torch.equal(lse.cpu(), l2.cpu())
+
+
+def test_kvcache_fp8():
+    case = fa_inputs.make_kvcache(2, 130, 70, 1024, [0, 400], 4, 2, 128, causal=True, seed=86,
+                                  dtype="e4m3")
+    kvcache_check(case, "kv_fp8")
