@@ -142,6 +142,85 @@ def copy_calibration(nbytes: int) -> None:
     log(f"copied {nbytes} bytes x3")
 
 
+# KV-cache decode: one new token per sequence appended to a long cache, then attention of
+# that token over the whole cache (bottom-right causal).  Bound by HBM: the cache is read once.
+KVCACHE_WORKLOADS = {
+    "kvcache_decode_b32_hq32_hkv8_c8192_d128": dict(batch=32, heads_q=32, heads_kv=8,
+                                                    capacity=8192, head_dim=128, seed=90),
+}
+HBM_PEAK_GBPS = 8000.0
+
+
+def run_kvcache(args, cfg) -> int:
+    """One step = fa_fwd_kvcache appending 1 row per sequence at position capacity-1 (the same
+    row every step) and attending over all `capacity` rows."""
+    import torch
+
+    import fa_inputs
+    import exact_attention_forward_fa_amd as fa
+
+    b, hq, hkv, cap, d = cfg["batch"], cfg["heads_q"], cfg["heads_kv"], cfg["capacity"], cfg["head_dim"]
+    case = fa_inputs.make_kvcache(b, 1, 1, cap, [cap - 1] * b, hq, hkv, d, causal=True,
+                                  seed=cfg["seed"])
+    log(f"workload {args.workload}: KV-cache decode, batch={b} hq={hq} hkv={hkv} cache={cap} d={d}")
+    q, kc, vc = case.q.cuda(), case.k_cache.cuda(), case.v_cache.cuda()
+    kn, vn = case.k_new.cuda(), case.v_new.cuda()
+    lens = torch.from_numpy(case.cache_seqlens).cuda()
+    o = torch.empty((b, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, b), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fa_fwd_kvcache(q, kc, vc, kn, vn, o, lse, b, hq, hkv, 1, 1, cap, lens, d, d,
+                          case.softmax_scale, 1, None, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    flops = 2 * (d + d) * hq * b * cap  # each query row sees all `cap` keys
+    # algorithmic bytes: the used cache rows of K and V read once, Q in, O and LSE out, the
+    # appended K/V rows read and written
+    hbm = 2 * b * cap * hkv * d * 2 + b * hq * d * 2 * 2 + b * hq * 4 + 2 * 2 * b * hkv * d * 2
+    gbps = hbm / (step_ms * 1e-3) / 1e9
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    log(f"step {step_ms:.4f} ms (events: append + attention), {gbps:.0f} GB/s = "
+        f"{100 * gbps / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f} GB/s, {value:.2f} TFLOPS")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
+        "config": {"workload": args.workload, "batch": b, "heads_q": hq, "heads_kv": hkv,
+                   "seqlen_q": 1, "seqlen_new": 1, "cache_capacity": cap, "head_dim": d,
+                   "causal": True, "flops_per_step": flops, "hbm_bytes_per_step": hbm},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel_ms": round(step_ms, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +252,8 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.workload in KVCACHE_WORKLOADS:
+        return run_kvcache(args, KVCACHE_WORKLOADS[args.workload])
     w = fa_inputs.workload(args.workload)
     log(f"workload {w.name}: batch={w.batch} hq={w.heads_q} hkv={w.heads_kv} sq={w.seqlen_q} "
         f"sk={w.seqlen_k} d={w.head_dim} causal={w.causal} dtype={w.dtype}")
