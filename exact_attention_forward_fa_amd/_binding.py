@@ -46,7 +46,8 @@ class Plan(ctypes.Structure):
                 ("kv_stages", ctypes.c_int), ("lds_bytes", ctypes.c_int64),
                 ("wg_per_cu", ctypes.c_int), ("vgprs_per_lane", ctypes.c_int),
                 ("num_workgroups", ctypes.c_int64), ("m_tiles", ctypes.c_int),
-                ("kernel_variant", ctypes.c_int), ("query_tiles", ctypes.c_int)]
+                ("kernel_variant", ctypes.c_int), ("query_tiles", ctypes.c_int),
+                ("heads_per_workgroup", ctypes.c_int), ("schedule", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -81,8 +82,8 @@ def _load():
                                 ctypes.POINTER(DeviceLimits), ctypes.POINTER(Plan)]
     lib.fa_fwd_plan.restype = i32
     lib.fa_version.restype = i32
-    lib.fa_set_query_tiles.argtypes = [i32]
-    lib.fa_set_query_tiles.restype = i32
+    lib.fa_set_schedule.argtypes = [i32]
+    lib.fa_set_schedule.restype = i32
     lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                    i32, i32, ctypes.c_float, i32, vp, vp]
     lib.fa_fwd_kvcache.restype = i32
@@ -100,11 +101,12 @@ def fa_version() -> int:
     return int(_lib.fa_version())
 
 
-def fa_set_query_tiles(query_tiles: int) -> None:
-    """Tuning override of the bf16 tiling: 0 automatic, 1 or 2 query tiles of 32 rows per wave."""
-    rc = _lib.fa_set_query_tiles(int(query_tiles))
+def fa_set_schedule(schedule: int) -> None:
+    """Tuning override of the planner: 0 automatic; 1 one query tile per wave; 2 two query tiles
+    per wave (bf16); 3 the 8-wave ping-pong (bf16, even heads_q / heads_kv)."""
+    rc = _lib.fa_set_schedule(int(schedule))
     if rc != 0:
-        raise FaError(rc, "fa_set_query_tiles")
+        raise FaError(rc, "fa_set_schedule")
 
 
 def fa_gfx950_limits() -> DeviceLimits:

@@ -16,8 +16,8 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// fa_set_query_tiles: 0 automatic, else the forced bf16 query tiles per wave
-std::atomic<int> g_query_tiles{0};
+// fa_set_schedule: 0 automatic, else the forced schedule (1, 2 or 3)
+std::atomic<int> g_schedule{0};
 
 // gfx950 (MI355X): 160 KiB LDS per CU, all of it addressable by one
 // workgroup; 256 CUs; 4 SIMDs per CU; 512 VGPR+AGPR per lane per SIMD;
@@ -50,9 +50,9 @@ const char* fa_strerror(int code) {
   }
 }
 
-int fa_set_query_tiles(int query_tiles) {
-  if (query_tiles < 0 || query_tiles > 2) return FA_ERR_INVALID;
-  g_query_tiles.store(query_tiles, std::memory_order_relaxed);
+int fa_set_schedule(int schedule) {
+  if (schedule < 0 || schedule > 3) return FA_ERR_INVALID;
+  g_schedule.store(schedule, std::memory_order_relaxed);
   return FA_OK;
 }
 
@@ -96,37 +96,50 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   if (L.lds_bytes_per_block <= 0 || L.lds_bytes_per_cu <= 0 || L.simds_per_cu <= 0 ||
       L.regs_per_simd_lane <= 0)
     return FA_ERR_INVALID;
-  // The compiled kernels: 4 waves per workgroup, each wave holding QT query
-  // tiles of 32 rows (Q in registers), 64-key blocks, K/V double-buffered in
-  // LDS without padding.  QT = 1: 128 rows per workgroup, 256 registers per
-  // lane (2 waves per SIMD).  QT = 2 (bf16): 256 rows per workgroup, the full
-  // 512-register file (1 wave per SIMD); each LDS operand read feeds two
-  // MFMAs.  The automatic choice is QT = 1 (measured faster on every
-  // workload so far: with one wave per SIMD nothing hides the softmax's
-  // serial steps); QT = 2 is reachable through fa_set_query_tiles.
+  // The compiled kernels (64-key blocks, Q in registers, K/V double-buffered
+  // in LDS without padding):
+  //  * schedule 1: 4 waves, one 32-row query tile each: 128 rows of one head
+  //    per workgroup, 256 registers per lane (2 waves per SIMD);
+  //  * schedule 2 (bf16): 4 waves with two query tiles each: 256 rows of one
+  //    head, the full 512-register file (1 wave per SIMD); each LDS operand
+  //    read feeds two MFMAs;
+  //  * schedule 3 (bf16, heads_q / heads_kv even): 8 waves in two groups of
+  //    four, 128 rows of two query heads that share a KV head, alternating
+  //    GEMM and softmax slots (ping-pong), 256 registers per lane.
+  // Automatic: schedule 3 where it applies, else 1.  fa_set_schedule forces
+  // one (falling back to 1 where the forced one does not apply).
   const int64_t lds = fa::lds_bytes(head_dim, dtype == FA_DTYPE_E4M3 ? 1 : 2);
   if (lds > L.lds_bytes_per_block) return FA_ERR_UNSUPPORTED;
   const int64_t pairs = (int64_t)batch * heads_kv;
   const int64_t rounds = (pairs + fa::kXcds - 1) / fa::kXcds;
-  const int forced = g_query_tiles.load(std::memory_order_relaxed);
-  const bool wide_ok = dtype == FA_DTYPE_BF16 && L.regs_per_simd_lane >= 512;
-  const int qt = wide_ok && forced ? forced : 1;
+  const int group = heads_q / heads_kv;
+  const bool bf16 = dtype == FA_DTYPE_BF16;
+  const bool wide_ok = bf16 && L.regs_per_simd_lane >= 512;
+  const bool pp_ok = bf16 && group % 2 == 0 && L.regs_per_simd_lane >= 512;
+  const int forced = g_schedule.load(std::memory_order_relaxed);
+  int sched = forced ? forced : (pp_ok ? 3 : 1);
+  if ((sched == 2 && !wide_ok) || (sched == 3 && !pp_ok)) sched = 1;
+  const int qt = sched == 2 ? 2 : 1;
+  const int waves = sched == 3 ? 2 * fa::kWaves : fa::kWaves;
+  const int heads_per_wg = sched == 3 ? 2 : 1;
   const int vgprs = 256 * qt;
   const int by_lds = (int)(L.lds_bytes_per_cu / lds);
-  const int by_regs = (L.regs_per_simd_lane / vgprs) * L.simds_per_cu / fa::kWaves;
+  const int by_regs = (L.regs_per_simd_lane / vgprs) * L.simds_per_cu / waves;
   out->tile_m = fa::kTileM * qt;
   out->tile_n = fa::kTileN;
-  out->waves = fa::kWaves;
+  out->waves = waves;
   out->kv_stages = fa::kStages;
   out->lds_bytes = lds;
   out->wg_per_cu = by_lds < by_regs ? by_lds : by_regs;
   out->vgprs_per_lane = vgprs;
   out->query_tiles = qt;
+  out->heads_per_workgroup = heads_per_wg;
+  out->schedule = sched;
   out->m_tiles = (seqlen_q + out->tile_m - 1) / out->tile_m;
-  // one slot per (query tile, query head) of every (sequence, kv-head) pair,
-  // the pairs dealt round-robin to the XCDs (the last round padded)
+  // one slot per (query tile, query head or head pair) of every (sequence,
+  // kv-head) pair, the pairs dealt round-robin to the XCDs (the last round padded)
   out->num_workgroups = out->m_tiles == 0 ? 0
-                        : rounds * fa::kXcds * out->m_tiles * (int64_t)(heads_q / heads_kv);
+                        : rounds * fa::kXcds * out->m_tiles * (int64_t)(group / heads_per_wg);
   out->kernel_variant = (head_dim == 128 ? 0 : 2) + (causal ? 1 : 0) + (dtype == FA_DTYPE_E4M3 ? 4 : 0);
   if (out->wg_per_cu <= 0) return FA_ERR_UNSUPPORTED;
   return FA_OK;
@@ -190,6 +203,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   L.fp8 = dtype == FA_DTYPE_E4M3;
   L.num_workgroups = plan.num_workgroups;
   L.query_tiles = qt;
+  L.pingpong = plan.schedule == 3;
   return fa::launch(L, stream);
 }
 

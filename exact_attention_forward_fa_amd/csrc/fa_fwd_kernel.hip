@@ -540,6 +540,294 @@ void fa_fwd_bf16_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Ping-pong schedule (bf16; heads_q / heads_kv even).  A workgroup of 8 waves
+// (two per SIMD) takes one 128-row query tile of TWO query heads that share a
+// KV head, so both halves walk the same key blocks out of one K/V staging.
+// Waves 0-3 (group A, first head) and 4-7 (group B, second head) alternate
+// between a GEMM slot -- the QK^T of the next block and the P V of the current
+// one, with all their LDS operand reads -- and a softmax slot (VALU and the
+// transcendental unit only), offset by one slot: while one wave of a SIMD
+// keeps the matrix core busy, the other exponentiates.  Slots are separated
+// by workgroup barriers.  Step k (k = 0 .. N, N key blocks, block N-1-k is
+// the one whose scores step k computes):
+//   slot 2k:   A: GEMM(k)            B: softmax of block N-k (k >= 1)
+//   slot 2k+1: A: softmax of N-1-k   B: GEMM(k)
+// GEMM(k) = S <- K_{N-1-k} Q^T (k < N) and O += V_{N-k}^T P^T (k >= 1).  K_j
+// lives in K buffer (N-1-j) & 1 and V_j in V buffer (N-1-j) & 1; at the start
+// of slot 2k all eight waves load K_{N-2-k} and V_{N-1-k}, two slots before
+// their first use, into the buffers whose last readers finished in slot 2k-1.
+#ifndef PP_AHEAD
+#define PP_AHEAD 20
+#endif
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_bf16_pp_kernel(Params p) {
+  constexpr int TM = kTileM, TN = kTileN;
+  constexpr int RB = D * 2;                  // bytes per K/V row in LDS
+  constexpr int BUF = TN * RB;               // bytes per K or V block buffer
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int NW = 8;                      // waves per workgroup
+  constexpr int NI = TN * CPR / (64 * NW);   // direct-load instructions per wave per block
+  constexpr int KC = D / 16;                 // k-chunks of the QK^T product
+  constexpr int DT = D / 32;                 // 32-wide output tiles of O^T
+  static_assert(NI >= 1, "each wave issues at least one load per block");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * BUF];
+  char* const kbuf0 = smem;
+  char* const vbuf0 = smem + 2 * BUF;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int grp = wave >> 2;  // 0: group A, 1: group B
+  const int wv = wave & 3;    // 32-row slice of the tile
+  const int lane = tid & 63;
+  const int r32 = lane & 31;
+  const int hf = lane >> 5;
+
+  // ---- work item: the XCD deal of the 4-wave kernel, with pairs of query
+  // heads in place of query heads
+  const int hpairs = p.group >> 1;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per_pair = p.m_tiles * hpairs;
+  const int kk = slot / per_pair;
+  const int within = slot - kk * per_pair;
+  const int pair = xcd + kXcds * kk;
+  if (pair >= p.batch * p.hkv) return;  // padding of the last round
+  const int b = pair / p.hkv;
+  const int mrev = within / hpairs;
+  const int g = pair - b * p.hkv;
+  const int head = g * p.group + 2 * (within - mrev * hpairs) + grp;
+  const int mblk = CAUSAL ? (p.m_tiles - 1 - mrev) : mrev;
+  const SeqInfo si = seq_info(p, b);
+  const int m0 = mblk * TM;
+  if (m0 >= si.sq) return;  // uniform over the workgroup, before any barrier
+  const int qi = m0 + wv * 32 + r32;
+  const bool qvalid = qi < si.sq;
+
+  const __bf16* __restrict__ Q = (const __bf16*)p.q;
+  __bf16* __restrict__ O = (__bf16*)p.o;
+  const float c = p.scale_log2;
+
+  const int diag = si.sk - si.sq;  // bottom-right alignment offset
+  int kend = si.sk;
+  if (CAUSAL) kend = min(kend, m0 + TM + diag);
+  const int N = kend > 0 ? (kend + TN - 1) / TN : 0;
+
+  auto orow = [&]() __attribute__((always_inline)) {
+    return ((int64_t)(si.q0 + qi) * p.hq + head) * D;
+  };
+  auto lse_idx = [&]() __attribute__((always_inline)) {
+    return (int64_t)head * si.total_q + si.q0 + qi;
+  };
+
+  if (N == 0) {  // store_zero
+    if (qvalid) {
+      for (int e = hf * 4; e < D; e += 8) *(u32x2*)(O + orow() + e) = u32x2{0u, 0u};
+      if (hf == 0) p.lse[lse_idx()] = -INFINITY;
+    }
+    return;
+  }
+
+  bf16x8 qf[KC];
+  {
+    const __bf16* qp = Q + orow() + 8 * hf;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 t = qvalid ? *(const u32x4*)(qp + 16 * kc) : u32x4{0u, 0u, 0u, 0u};
+      qf[kc] = __builtin_bit_cast(bf16x8, t);
+    }
+  }
+
+  // ---- K/V staging (as the 4-wave kernel; eight waves share each block)
+  const int key_stride_b = p.hkv * D * 2;
+  const char* kseq = (const char*)p.k + ((int64_t)si.k0 * p.hkv + g) * D * 2;
+  const char* vseq = (const char*)p.v + ((int64_t)si.k0 * p.hkv + g) * D * 2;
+  unsigned koff[NI], voff[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int P = (wave * NI + u) * 64 + lane;
+    const int row = P / CPR, pc = P % CPR;
+    koff[u] = (unsigned)(k_lds_row(row) * key_stride_b + ((pc ^ swz_k<D>(row)) * 16));
+    voff[u] = (unsigned)(row * key_stride_b + ((pc ^ swz_v<D>(row)) * 16));
+  }
+  const int wave_lds = __builtin_amdgcn_readfirstlane(wave * NI * 1024);
+  auto stage = [&](const char* seq, const unsigned* off, char* dst, int n) __attribute__((always_inline)) {
+    const int keys_left = si.sk - n * TN;  // > 0 for every staged block
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(seq + (int64_t)n * TN * key_stride_b), (short)0, keys_left * key_stride_b,
+        kRsrcWord3);
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + wave_lds + u * 1024), 16,
+                                               off[u], 0, 0, 0);
+  };
+
+  int ka[KC];
+  {
+    const int x = swz_k<D>(r32);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) ka[kc] = r32 * RB + (((2 * kc + hf) ^ x) * 16);
+  }
+  int va[DT];
+  {
+    const int tr_row = (lane & 15) >> 2;
+    const int lc_lo = ((lane >> 4) & 1) * 2 + ((lane & 3) >> 1);
+    const int half = (lane & 1) * 8;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int lc = 4 * t + lc_lo;
+      va[t] = (8 * hf + tr_row) * RB + ((lc ^ swz_v<D>(tr_row)) * 16) + half;
+    }
+  }
+
+  // ---- per-wave state: one score tile, one P tile, O, running max and sum
+  f32x16 sc[2];
+  bf16x8 pb[4];
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int thr = CAUSAL ? min(si.sk, m0 + diag + 1) : si.sk;
+  const int n_plain = thr <= 0 ? 0 : min(N, thr / TN);  // blocks below n_plain need no mask
+
+  // softmax slot for block j: mask, running max, lazy rescale, P and row sum
+  auto softmax = [&](const int j) __attribute__((always_inline)) {
+    if (j >= n_plain) {
+      const int lim = CAUSAL ? min(si.sk - 1, qi + diag) : si.sk - 1;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * TN + 32 * t + 16 * (r >> 3) + 8 * hf + (r & 7);
+          if (key > lim) sc[t][r] = -INFINITY;
+        }
+    }
+    const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy) != 0, 0)) {
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+    }
+    const float ms = (m_run == -INFINITY ? 0.f : m_run) * c;
+    float rs = 0.f;
+#pragma unroll
+    for (int idx = 0; idx < 32; ++idx) {
+      const int tt = idx >> 4, r = idx & 15;
+      const float pv = exp2_fast(__builtin_fmaf(sc[tt][r], c, -ms));
+      rs += pv;
+      pb[2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
+    }
+    l_run += rs;
+  };
+
+  // GEMM slot: QK of the next block and P V of the current one, interleaved
+  auto gemm = [&](const char* __restrict__ kread, const char* __restrict__ vread, auto qk_tag,
+                  auto pv_tag) __attribute__((always_inline)) {
+    constexpr bool DO_QK = decltype(qk_tag)::value;
+    constexpr bool DO_PV = decltype(pv_tag)::value;
+    if (DO_QK) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sc[t] = f32x16{};
+    }
+    constexpr int STEPS = 2 * KC > 4 * DT ? 2 * KC : 4 * DT;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      if (DO_QK && st < 2 * KC) {
+        const int kc = st >> 1, t = st & 1;
+        bf16x8 a = *(const bf16x8*)(kread + 32 * t * RB + ka[kc]);
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], sc[t], 0, 0, 0);
+      }
+      if (DO_PV && st < 4 * DT) {
+        const int kc2 = st / DT, t = st % DT;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vread + 16 * kc2 * RB + va[t]));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vread + (16 * kc2 + 4) * RB + va[t]));
+        bf16x4 lob = __builtin_bit_cast(bf16x4, lo), hib = __builtin_bit_cast(bf16x4, hi);
+        bf16x8 a = {lob[0], lob[1], lob[2], lob[3], hib[0], hib[1], hib[2], hib[3]};
+        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], oacc[t], 0, 0, 0);
+      }
+    }
+    if (DO_QK && DO_PV) {
+      // Only this wave of the SIMD issues MFMAs during the slot, so nothing
+      // else hides LDS latency: keep PP_AHEAD operand reads in flight.
+      sched_group(kSchedDsRead, PP_AHEAD);
+#pragma unroll
+      for (int i = 0; i < 2 * STEPS; ++i) {
+        sched_group(kSchedMfma, 1);
+        sched_group(kSchedDsRead, 1);
+      }
+    }
+  };
+
+  // One step: the full barrier (the loads issued two slots ago are complete
+  // and visible, the buffers read in slot 2k-1 are free), this step's loads,
+  // the two slots.  The barrier between the slots only orders the phases.
+  // The four LDS regions are distinct within a step; __restrict__ says so,
+  // which keeps the compiler from waiting for the loads before LDS reads.
+  auto step = [&](const int k, const char* __restrict__ kread, const char* __restrict__ vread,
+                  char* __restrict__ kdst, char* __restrict__ vdst, auto qk_tag, auto pv_tag)
+      __attribute__((always_inline)) {
+    __syncthreads();
+    if (N - 2 - k >= 0) stage(kseq, koff, kdst, N - 2 - k);
+    if (N - 1 - k >= 0) stage(vseq, voff, vdst, N - 1 - k);
+    if (grp == 0) {
+      gemm(kread, vread, qk_tag, pv_tag);
+    } else if (k >= 1) {
+      softmax(N - k);
+    }
+    asm volatile("s_barrier" ::: "memory");
+    if (grp == 0) {
+      if (k < N) softmax(N - 1 - k);
+    } else {
+      gemm(kread, vread, qk_tag, pv_tag);
+    }
+  };
+  auto bufs = [&](const int k, const char*& kr, const char*& vr, char*& kd, char*& vd)
+      __attribute__((always_inline)) {
+    const int par = k & 1;
+    kr = kbuf0 + par * BUF;
+    kd = kbuf0 + (par ^ 1) * BUF;
+    vr = vbuf0 + (par ^ 1) * BUF;
+    vd = vbuf0 + par * BUF;
+  };
+
+  stage(kseq, koff, kbuf0, N - 1);  // K_{N-1}: buffer 0
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  {
+    const char *kr, *vr;
+    char *kd, *vd;
+    bufs(0, kr, vr, kd, vd);
+    step(0, kr, vr, kd, vd, BoolTag<true>{}, BoolTag<false>{});
+    for (int k = 1; k < N; ++k) {
+      bufs(k, kr, vr, kd, vd);
+      step(k, kr, vr, kd, vd, BoolTag<true>{}, BoolTag<true>{});
+    }
+    bufs(N, kr, vr, kd, vd);
+    step(N, kr, vr, kd, vd, BoolTag<false>{}, BoolTag<true>{});
+  }
+
+  // ---- epilogue
+  pin_accumulators(oacc);
+  const float l_tot = halfwave_sum(l_run);
+  if (!qvalid) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 ov;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(oacc[t][4 * i4 + j] * inv);
+      *(bf16x4*)(O + orow() + 32 * t + 8 * i4 + 4 * hf) = ov;
+    }
+  if (hf == 0) p.lse[lse_idx()] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
 // FP8 (OCP e4m3) inputs.  Same tiling and pipeline as the bf16 kernel, on the
 // gfx950 fp8 MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (block scales fixed at
 // 2^0): each lane feeds 32 bytes of its row (A) or column (B); the 64 products
@@ -848,7 +1136,17 @@ void launch_fp8(const Launch& L, hipStream_t stream) {
 }
 
 template <int D, bool CAUSAL>
+void launch_bf16_pp(const Launch& L, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_bf16_pp_kernel<D, CAUSAL>), dim3((unsigned)L.num_workgroups),
+                     dim3(512), 0, stream, L.p);
+}
+
+template <int D, bool CAUSAL>
 void launch_bf16(const Launch& L, hipStream_t stream) {
+  if (L.pingpong) {
+    launch_bf16_pp<D, CAUSAL>(L, stream);
+    return;
+  }
   if (L.query_tiles == 2)
     hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, 2>), dim3((unsigned)L.num_workgroups),
                        dim3(256), 0, stream, L.p);

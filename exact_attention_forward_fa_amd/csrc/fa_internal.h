@@ -43,6 +43,7 @@ struct Launch {
   int causal;
   int fp8;
   int query_tiles;  // 32-row query tiles per wave (1 or 2)
+  int pingpong;     // 1: the 8-wave ping-pong kernel (bf16, two query heads per workgroup)
   int64_t num_workgroups;
 };
 

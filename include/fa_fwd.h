@@ -186,6 +186,8 @@ typedef struct fa_plan {
   int m_tiles;           /* query tiles per (sequence, head)                  */
   int kernel_variant;    /* index of the compiled kernel                      */
   int query_tiles;       /* 32-row query tiles per wave (tile_m = 128 * this) */
+  int heads_per_workgroup; /* query heads sharing one workgroup's K/V staging  */
+  int schedule;          /* 1, 2 or 3 (see fa_fwd_plan)                       */
 } fa_plan_t;
 
 /*
@@ -193,28 +195,35 @@ typedef struct fa_plan {
  * function, no HIP call).  dev == NULL means gfx950.  Returns FA_OK,
  * FA_ERR_NULL, FA_ERR_INVALID or FA_ERR_UNSUPPORTED (nothing fits `dev`).
  *
- * The plan uses query_tiles = 1 (128 query rows per workgroup, two waves per
- * SIMD) unless fa_set_query_tiles forces 2 for bf16 (256 rows per workgroup,
- * one wave per SIMD holding the full register file, every LDS operand read
- * feeding two matrix instructions).  fp8 always uses 1.
+ * Schedules:
+ *   1  4 waves, one 32-row query tile each: 128 rows of one query head per
+ *      workgroup, two waves per SIMD (every shape, bf16 and fp8);
+ *   2  bf16: 4 waves with two query tiles each: 256 rows of one head, one wave
+ *      per SIMD holding the full register file, every LDS operand read
+ *      feeding two matrix instructions;
+ *   3  bf16, heads_q / heads_kv even: 8 waves in two groups of four, 128 rows
+ *      of two query heads that share a KV head (one K/V staging for both),
+ *      the groups alternating matrix-core and softmax phases (ping-pong).
+ * The plan uses 3 where it applies, else 1, unless fa_set_schedule forces
+ * one.
  */
 int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
                 int varlen, int head_dim, int head_dim_v, int causal,
                 const fa_device_limits_t* dev, fa_plan_t* out);
 
 /*
- * fa_set_query_tiles -- tuning override of the planner's tiling choice for
- * bf16 (for benchmarking and for tests that exercise both tilings on the
- * same shapes).  0 restores the automatic choice; 1 or 2 forces that many
- * 32-row query tiles per wave in every later fa_fwd / fa_fwd_plan call of the
- * process (fp8 always uses 1).  Both tilings compute the same function to
+ * fa_set_schedule -- tuning override of the planner's schedule choice (for
+ * benchmarking and for tests that run every schedule on the same shapes).
+ * 0 restores the automatic choice; 1, 2 or 3 forces that schedule in every
+ * later fa_fwd / fa_fwd_kvcache / fa_fwd_plan call of the process wherever it
+ * applies (schedule 1 elsewhere).  All schedules compute the same function to
  * within rounding, but not bit for bit: the reference maximum that the
- * softmax rescales against is updated per wave, and a wave holds different
- * rows in the two tilings.  The setting is a process-wide atomic; calls
- * already launched are unaffected.  Returns FA_OK, or FA_ERR_INVALID for any
- * other value.
+ * softmax rescales against is updated per wave, and waves hold different rows
+ * in different schedules.  The setting is a process-wide atomic; calls already
+ * launched are unaffected.  Returns FA_OK, or FA_ERR_INVALID for any other
+ * value.
  */
-int fa_set_query_tiles(int query_tiles);
+int fa_set_schedule(int schedule);
 
 /* Library version: major*10000 + minor*100 + patch. */
 int fa_version(void);

@@ -190,42 +190,51 @@ def test_screen_rejects_bad_sizes():
 
 
 def test_plan_gfx950():
-    # one query tile per wave: 128 rows per workgroup, two waves per SIMD, two workgroups per CU
+    # GQA with an even group: the ping-pong schedule, 8 waves holding 128 rows of two query
+    # heads, one workgroup per CU (2 waves per SIMD at 256 registers)
     p = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 32, 8, 8192, 8192, False, 128, 128, True)
-    assert (p.tile_m, p.tile_n, p.waves, p.kv_stages, p.query_tiles) == (128, 64, 4, 2, 1)
-    assert p.lds_bytes == 64 * KIB and p.wg_per_cu == 2 and p.vgprs_per_lane == 256
-    # 16 (batch, kv-head) pairs = 2 rounds over 8 XCDs, x 64 tiles x 4 query heads per kv-head
-    assert p.m_tiles == 64 and p.num_workgroups == 2 * 8 * 64 * 4
+    assert (p.schedule, p.tile_m, p.tile_n, p.waves, p.kv_stages) == (3, 128, 64, 8, 2)
+    assert (p.query_tiles, p.heads_per_workgroup, p.wg_per_cu, p.vgprs_per_lane) == (1, 2, 1, 256)
+    assert p.lds_bytes == 64 * KIB
+    # 16 (batch, kv-head) pairs = 2 rounds over 8 XCDs, x 64 tiles x 2 head pairs per kv-head
+    assert p.m_tiles == 64 and p.num_workgroups == 2 * 8 * 64 * 2
     p64 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 2, 2, 256, 256, False, 64, 64, False)
-    # small shape: one query tile per wave; 2 (batch, kv-head) pairs dealt to 8 XCDs: one
-    # padded round of 8 pairs x 2 tiles x 1 head
-    assert (p64.tile_m, p64.query_tiles, p64.wg_per_cu, p64.vgprs_per_lane) == (128, 1, 2, 256)
+    # heads_q / heads_kv = 1: one query tile per wave; 2 (batch, kv-head) pairs dealt to 8
+    # XCDs: one padded round of 8 pairs x 2 tiles x 1 head
+    assert (p64.schedule, p64.tile_m, p64.query_tiles, p64.wg_per_cu, p64.vgprs_per_lane) == \
+        (1, 128, 1, 2, 256)
     assert p64.m_tiles == 2 and p64.num_workgroups == 8 * 2 and p64.lds_bytes < p.lds_bytes
-    # fp8 always uses one query tile per wave
-    p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 32, 32, 16384, 16384, False, 128, 128, True)
-    assert (p8.tile_m, p8.query_tiles, p8.lds_bytes) == (128, 1, 32 * KIB)
+    # fp8 always uses schedule 1
+    p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 32, 8, 16384, 16384, False, 128, 128, True)
+    assert (p8.schedule, p8.tile_m, p8.query_tiles, p8.lds_bytes) == (1, 128, 1, 32 * KIB)
 
 
-def test_query_tiles_override():
+def test_schedule_override():
     args = (fa.FA_DTYPE_BF16, 2, 32, 8, 8192, 8192, False, 128, 128, True)
     try:
-        fa.fa_set_query_tiles(2)
+        fa.fa_set_schedule(1)
         p = fa.fa_fwd_plan(*args)
-        assert (p.tile_m, p.query_tiles, p.m_tiles, p.wg_per_cu, p.vgprs_per_lane) == (256, 2, 32, 1, 512)
+        assert (p.schedule, p.tile_m, p.waves, p.m_tiles, p.wg_per_cu) == (1, 128, 4, 64, 2)
+        assert p.num_workgroups == 2 * 8 * 64 * 4
+        fa.fa_set_schedule(2)
+        p = fa.fa_fwd_plan(*args)
+        assert (p.schedule, p.tile_m, p.query_tiles, p.m_tiles, p.wg_per_cu, p.vgprs_per_lane) == \
+            (2, 256, 2, 32, 1, 512)
         assert p.num_workgroups == 2 * 8 * 32 * 4
-        small = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 2, 2, 300, 300, False, 64, 64, False)
-        assert (small.tile_m, small.query_tiles, small.m_tiles) == (256, 2, 2)
-        p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 2, 2, 300, 300, False, 64, 64, False)
-        assert p8.query_tiles == 1
-        for bad in (-1, 3):
+        # schedule 3 needs an even heads_q / heads_kv: falls back to 1
+        fa.fa_set_schedule(3)
+        odd = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 3, 1, 300, 300, False, 64, 64, False)
+        assert (odd.schedule, odd.waves, odd.heads_per_workgroup) == (1, 4, 1)
+        # fp8 always uses 1
+        p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 2, 1, 300, 300, False, 64, 64, False)
+        assert p8.schedule == 1
+        for bad in (-1, 4):
             with pytest.raises(fa.FaError) as e:
-                fa.fa_set_query_tiles(bad)
+                fa.fa_set_schedule(bad)
             assert e.value.code == fa.FA_ERR_INVALID
-        fa.fa_set_query_tiles(1)
-        assert fa.fa_fwd_plan(*args).query_tiles == 1
     finally:
-        fa.fa_set_query_tiles(0)
-    assert fa.fa_fwd_plan(*args).query_tiles == 1
+        fa.fa_set_schedule(0)
+    assert fa.fa_fwd_plan(*args).schedule == 3
 
 
 def test_plan_reports_unsupported_when_nothing_fits():

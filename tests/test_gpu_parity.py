@@ -11,14 +11,15 @@ from parity import compare, gather_rows, gpu_run, oracle_full, oracle_rows, samp
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=[1, 2], ids=["qt1", "qt2"])
-def query_tiles(request):
-    """Force each bf16 tiling (1 or 2 query tiles of 32 rows per wave) for the test."""
+@pytest.fixture(params=[1, 2, 3], ids=["sched1", "sched2", "sched3"])
+def schedule(request):
+    """Force each bf16 schedule (1: one query tile per wave; 2: two; 3: 8-wave ping-pong,
+    where heads_q / heads_kv is even, else 1) for the test."""
     import exact_attention_forward_fa_amd as fa
 
-    fa.fa_set_query_tiles(request.param)
+    fa.fa_set_schedule(request.param)
     yield request.param
-    fa.fa_set_query_tiles(0)
+    fa.fa_set_schedule(0)
 
 
 def full_check(w):
@@ -45,7 +46,7 @@ def test_tiny_noncausal_d64():
 
 
 @pytest.mark.parametrize("name", ["mha_b4_h16_s1024_d128", "mha_causal_b4_h16_s1024_d128"])
-def test_mha_1024(name, query_tiles):
+def test_mha_1024(name, schedule):
     full_check(fa_inputs.workload(name))
 
 
@@ -56,15 +57,15 @@ def test_gqa_causal_8192_sampled():
 
 
 def test_gqa_causal_8192_sampled_one_tile_per_wave():
-    """The same workload through the 128-row tiling (the planner picks 256 rows for it)."""
+    """The same workload through schedule 1 (the planner picks the ping-pong for it)."""
     import exact_attention_forward_fa_amd as fa
 
     w = fa_inputs.workload("gqa_causal_b2_hq32_hkv8_s8192_d128")
-    fa.fa_set_query_tiles(1)
+    fa.fa_set_schedule(1)
     try:
         o, lse = sampled_check(w, n_random=16)
     finally:
-        fa.fa_set_query_tiles(0)
+        fa.fa_set_schedule(0)
     assert np.isfinite(lse).all() and np.isfinite(o).all()
 
 
@@ -81,7 +82,7 @@ def test_varlen_causal_sampled():
         assert np.all(np.isfinite(lse[:, q0 + dead:q0 + sq]))
 
 
-def test_varlen_equals_per_sequence_calls(query_tiles):
+def test_varlen_equals_per_sequence_calls(schedule):
     """Packed varlen output equals separate fixed-length calls, bit for bit (same tiling)."""
     lens = [(300, 517), (1, 64), (129, 100), (64, 0), (0, 40), (255, 256), (70, 700)]
     w = fa_inputs.make(0, 4, 2, 0, 0, 128, causal=True, seed=50, lengths=lens, name="varlen_small")
@@ -110,10 +111,10 @@ def test_varlen_equals_per_sequence_calls(query_tiles):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 4, 4, 300, 300), (1, 8, 2, 200, 517), (1, 4, 1, 517, 200),
                                    (3, 2, 2, 1, 1), (1, 2, 2, 1, 333), (1, 32, 1, 130, 130)])
-def test_ragged_shapes(shape, causal, d, query_tiles):
+def test_ragged_shapes(shape, causal, d, schedule):
     b, hq, hkv, sq, sk = shape
     w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq * 7 + sk + d,
-                       name=f"ragged_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}_c{int(causal)}_qt{query_tiles}")
+                       name=f"ragged_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}_c{int(causal)}_s{schedule}")
     full_check(w)
 
 
@@ -123,12 +124,12 @@ def test_seqlen_k_zero():
     assert np.all(o == 0.0) and np.all(lse == -np.inf)
 
 
-def test_large_q_magnitude(query_tiles):
+def test_large_q_magnitude(schedule):
     w = fa_inputs.make(1, 4, 4, 256, 256, 128, causal=True, seed=61, q_mult=50.0, name="q_x50")
     full_check(w)
 
 
-def test_gqa_equals_repeated_mha_on_gpu(query_tiles):
+def test_gqa_equals_repeated_mha_on_gpu(schedule):
     w = fa_inputs.make(1, 8, 2, 257, 257, 128, causal=True, seed=62, name="gqa")
     o1, l1 = gpu_run(w)
     w2 = fa_inputs.make(1, 8, 2, 257, 257, 128, causal=True, seed=62, name="gqa_as_mha")
@@ -139,7 +140,7 @@ def test_gqa_equals_repeated_mha_on_gpu(query_tiles):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_deterministic(query_tiles):
+def test_deterministic(schedule):
     w = fa_inputs.make(2, 8, 2, 700, 700, 128, causal=True, seed=63, name="det")
     t = to_device(w)
     o1, l1 = gpu_run(w, t)
@@ -147,7 +148,7 @@ def test_deterministic(query_tiles):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_no_writes_outside_outputs(query_tiles):
+def test_no_writes_outside_outputs(schedule):
     """Outputs carved from larger buffers filled with a sentinel: nothing past the ends changes."""
     import exact_attention_forward_fa_amd as fa
 
@@ -232,21 +233,21 @@ def kvcache_check(case, name):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_kvcache_decode_gqa(causal, query_tiles):
+def test_kvcache_decode_gqa(causal, schedule):
     """One new token per sequence, cache lengths from empty to exactly full."""
     case = fa_inputs.make_kvcache(4, 1, 1, 4096, [0, 1000, 4095, 2047], 8, 2, 128, causal=causal,
                                   seed=80)
-    kvcache_check(case, f"kv_decode_c{int(causal)}_qt{query_tiles}")
+    kvcache_check(case, f"kv_decode_c{int(causal)}_s{schedule}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_kvcache_prefill_chunk(causal, d, query_tiles):
+def test_kvcache_prefill_chunk(causal, d, schedule):
     """A 300-row chunk appended behind a prefix; the second sequence overflows the cache, so
     its last new rows are dropped and its length clamps to the capacity."""
     case = fa_inputs.make_kvcache(2, 300, 300, 2048, [100, 1900], 4, 4, d, causal=causal,
                                   seed=81 + d)
-    kvcache_check(case, f"kv_chunk_d{d}_c{int(causal)}_qt{query_tiles}")
+    kvcache_check(case, f"kv_chunk_d{d}_c{int(causal)}_s{schedule}")
 
 
 def test_kvcache_no_new_rows():
