@@ -152,6 +152,43 @@ __host__ __device__ __forceinline__ void pin_accumulators_agpr(f32x16 (&acc)[N])
 #endif
 }
 
+// O rows out of the O^T accumulator tiles.  Lane (query, hf) holds dims
+// 32t + 8i + 4hf + 0..3 of its query's row; one swap across the half-waves per
+// dword gives the low lane dims 32t + 16j + 0..7 and the high lane dims
+// 32t + 16j + 8..15, so every lane stores 16 contiguous bytes (half the store
+// instructions and twice the bytes per row per instruction of 8-byte stores).
+// All 64 lanes must be active (the two lanes of a query share `valid`).
+template <int DT>
+__device__ __forceinline__ void store_o_rows(const f32x16 (&acc)[DT], float scale, __bf16* row,
+                                             int hf, bool valid) {
+  u32x4 ost[DT][2];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x4 e, f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        e[x] = (__bf16)(acc[t][8 * j + x] * scale);
+        f[x] = (__bf16)(acc[t][8 * j + 4 + x] * scale);
+      }
+      u32x2 eu = __builtin_bit_cast(u32x2, e), fu = __builtin_bit_cast(u32x2, f);
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const auto r = __builtin_amdgcn_permlane32_swap(eu[w], fu[w], false, false);
+        eu[w] = r[0];
+        fu[w] = r[1];
+      }
+      ost[t][j] = u32x4{eu[0], eu[1], fu[0], fu[1]};
+    }
+  if (valid) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *(u32x4*)(row + 32 * t + 16 * j + 8 * hf) = ost[t][j];
+  }
+}
+
 // LDS layout of a 64-key block (K or V): 64 rows of D*2 bytes, no padding.
 // 16-byte column `lc` of row `r` is stored at physical column lc ^ swz(r):
 //  * K rows are read 16 B per lane by 16 consecutive rows at one column per
@@ -523,18 +560,9 @@ void fa_fwd_bf16_kernel(Params p) {
 #pragma unroll
   for (int q = 0; q < QG; ++q) {
     const float l_tot = halfwave_sum(l_run[q]);
-    if (!qvalid[q]) continue;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 ov;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(oacc[q][t][4 * i4 + j] * inv);
-        *(bf16x4*)(O + orow[q] + 32 * t + 8 * i4 + 4 * hf) = ov;
-      }
-    if (hf == 0)
+    store_o_rows<DT>(oacc[q], inv, O + orow[q], hf, qvalid[q]);
+    if (qvalid[q] && hf == 0)
       p.lse[lse_idx[q]] = l_tot > 0.f ? (m_run[q] * c + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
@@ -813,18 +841,10 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   // ---- epilogue
   pin_accumulators(oacc);
   const float l_tot = halfwave_sum(l_run);
-  if (!qvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      bf16x4 ov;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(oacc[t][4 * i4 + j] * inv);
-      *(bf16x4*)(O + orow() + 32 * t + 8 * i4 + 4 * hf) = ov;
-    }
-  if (hf == 0) p.lse[lse_idx()] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+  store_o_rows<DT>(oacc, inv, O + orow(), hf, qvalid);
+  if (qvalid && hf == 0)
+    p.lse[lse_idx()] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -1115,18 +1135,10 @@ void fa_fwd_fp8_kernel(Params p) {
 
   pin_accumulators(oacc);
   const float l_tot = halfwave_sum(l_run);
-  if (!qvalid) return;
   const float inv = l_tot > 0.f ? dvs / l_tot : 0.f;
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      bf16x4 ov;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(oacc[t][4 * i4 + j] * inv);
-      *(bf16x4*)(O + qrow + 32 * t + 8 * i4 + 4 * hf) = ov;
-    }
-  if (hf == 0) p.lse[lse_idx] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+  store_o_rows<DT>(oacc, inv, O + qrow, hf, qvalid);
+  if (qvalid && hf == 0)
+    p.lse[lse_idx] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL>
