@@ -16,7 +16,7 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// fa_set_schedule: 0 automatic, else the forced schedule (1, 2 or 3)
+// fa_set_schedule: 0 automatic, else the forced schedule (1 .. 4)
 std::atomic<int> g_schedule{0};
 
 // gfx950 (MI355X): 160 KiB LDS per CU, all of it addressable by one
@@ -51,7 +51,7 @@ const char* fa_strerror(int code) {
 }
 
 int fa_set_schedule(int schedule) {
-  if (schedule < 0 || schedule > 3) return FA_ERR_INVALID;
+  if (schedule < 0 || schedule > 4) return FA_ERR_INVALID;
   g_schedule.store(schedule, std::memory_order_relaxed);
   return FA_OK;
 }
@@ -105,9 +105,14 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   //    read feeds two MFMAs;
   //  * schedule 3 (bf16, heads_q / heads_kv even): 8 waves in two groups of
   //    four, 128 rows of two query heads that share a KV head, alternating
-  //    GEMM and softmax slots (ping-pong), 256 registers per lane.
-  // Automatic: schedule 3 where it applies, else 1.  fa_set_schedule forces
-  // one (falling back to 1 where the forced one does not apply).
+  //    GEMM and softmax slots (ping-pong), 256 registers per lane;
+  //  * schedule 4 (bf16, heads_q / heads_kv * seqlen_q <= 32): decode -- all
+  //    query rows of one KV head's group in the 32 columns of one tile, one
+  //    workgroup per (sequence, KV head) whose 4 waves split the key range in
+  //    32-key blocks, each with a 4-slot K register / V LDS ring, 512
+  //    registers per lane (one wave per SIMD).
+  // Automatic: 4 where it applies, else 3 where it applies, else 1.
+  // fa_set_schedule forces one (falling back to 1 where it does not apply).
   const int64_t lds = fa::lds_bytes(head_dim, dtype == FA_DTYPE_E4M3 ? 1 : 2);
   if (lds > L.lds_bytes_per_block) return FA_ERR_UNSUPPORTED;
   const int64_t pairs = (int64_t)batch * heads_kv;
@@ -116,9 +121,28 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const bool bf16 = dtype == FA_DTYPE_BF16;
   const bool wide_ok = bf16 && L.regs_per_simd_lane >= 512;
   const bool pp_ok = bf16 && group % 2 == 0 && L.regs_per_simd_lane >= 512;
+  const int64_t decode_lds = 4LL * fa::kDecodeSlots * 32 * head_dim * 2;
+  const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&
+                         L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;
   const int forced = g_schedule.load(std::memory_order_relaxed);
-  int sched = forced ? forced : (pp_ok ? 3 : 1);
-  if ((sched == 2 && !wide_ok) || (sched == 3 && !pp_ok)) sched = 1;
+  int sched = forced ? forced : (decode_ok ? 4 : pp_ok ? 3 : 1);
+  if ((sched == 2 && !wide_ok) || (sched == 3 && !pp_ok) || (sched == 4 && !decode_ok)) sched = 1;
+  if (sched == 4) {
+    out->tile_m = 32;  // (query head, row) columns of one tile
+    out->tile_n = 32;
+    out->waves = 4;
+    out->kv_stages = fa::kDecodeSlots;
+    out->lds_bytes = decode_lds;
+    out->wg_per_cu = 1;
+    out->vgprs_per_lane = 512;
+    out->query_tiles = 1;
+    out->heads_per_workgroup = group;
+    out->schedule = 4;
+    out->m_tiles = seqlen_q > 0 ? 1 : 0;
+    out->num_workgroups = out->m_tiles == 0 ? 0 : (int64_t)batch * heads_kv;
+    out->kernel_variant = (head_dim == 128 ? 0 : 2) + (causal ? 1 : 0);
+    return FA_OK;
+  }
   const int qt = sched == 2 ? 2 : 1;
   const int waves = sched == 3 ? 2 * fa::kWaves : fa::kWaves;
   const int heads_per_wg = sched == 3 ? 2 : 1;
@@ -204,6 +228,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   L.num_workgroups = plan.num_workgroups;
   L.query_tiles = qt;
   L.pingpong = plan.schedule == 3;
+  L.decode = plan.schedule == 4;
   return fa::launch(L, stream);
 }
 

@@ -848,6 +848,250 @@ void fa_fwd_bf16_pp_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Decode schedule (bf16; heads_q / heads_kv * seqlen_q <= 32).  Every query
+// row of one KV head's group -- the (query head, row) pairs -- fits the 32
+// columns of one MFMA tile, so a workgroup takes one (sequence, KV head) whole
+// and its four waves split the key range instead: wave w takes the 32-key
+// blocks w, w+4, w+8, ... Each wave streams its K blocks straight into
+// registers (in the A-operand order, rows permuted as k_lds_row lays them out
+// for the other kernels) and its V blocks through a private LDS ring, DEPTH
+// blocks ahead, so the loop has no barrier.  Each wave keeps the running
+// maximum, sum and O of the online softmax over its own blocks ([FWD-PASS]
+// consumer loop); the four partial states merge at the end through LDS with
+// the same rescaling the recurrence uses between blocks: with M the largest
+// partial maximum, O = sum_w 2^{c(m_w - M)} O_w / sum_w 2^{c(m_w - M)} l_w.
+// The work per key is small (at most 32 useful columns), so the kernel is
+// bound by streaming K and V from HBM.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_fwd_bf16_decode_kernel(Params p) {
+  constexpr int TK = 32;                 // keys per block
+  constexpr int RB = D * 2;              // bytes per K/V row
+  constexpr int VBUF = TK * RB;          // one V block in LDS
+  constexpr int NSTG = kDecodeSlots;     // K register slots and V ring slots per wave
+  constexpr int DEPTH = NSTG - 1;        // blocks loading while one is in use
+  constexpr int KC = D / 16;             // k-chunks of QK^T
+  constexpr int DT = D / 32;             // 32-dim tiles of O^T
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int NWV = 4;                 // waves
+  constexpr int VI = TK * CPR / 64;      // direct-load instructions per V block
+  constexpr int BLK_LOADS = KC + VI;     // memory instructions per block and wave
+  static_assert(DEPTH * BLK_LOADS <= 63, "vmcnt counts up to 63");
+  static_assert(NWV * (DT * 4096 + 512) <= NWV * NSTG * VBUF, "the merge area fits the rings");
+  __shared__ __attribute__((aligned(1024))) char smem[NWV * NSTG * VBUF];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r32 = lane & 31;
+  const int hf = lane >> 5;
+  char* const ring = smem + wave * (NSTG * VBUF);
+
+  const int b = blockIdx.x / p.hkv;
+  const int g = blockIdx.x - b * p.hkv;
+  const SeqInfo si = seq_info(p, b);
+  if (si.sq <= 0) return;  // uniform: no query rows
+  // this lane's column: query head g*group + hloc, query row qrow
+  const int hloc = r32 / si.sq;
+  const int qrow = r32 - hloc * si.sq;
+  const bool cvalid = hloc < p.group;
+  const int head = g * p.group + hloc;
+  const float c = p.scale_log2;
+  const int diag = si.sk - si.sq;  // bottom-right alignment offset
+  // the last query row sees every key (bottom-right alignment), so all
+  // ceil(sk / TK) blocks are read
+  const int nb = si.sk > 0 ? (si.sk + TK - 1) / TK : 0;
+  const int nmine = nb > wave ? (nb - wave + NWV - 1) / NWV : 0;
+  const int lim = CAUSAL ? min(si.sk - 1, qrow + diag) : si.sk - 1;  // last key of this column
+
+  // Q^T as the B operand: lane (column, hf) holds dims 16kc + 8hf .. +7
+  bf16x8 qf[KC];
+  {
+    const __bf16* qp = (const __bf16*)p.q + ((int64_t)(si.q0 + qrow) * p.hq + head) * D + 8 * hf;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 t = cvalid ? *(const u32x4*)(qp + 16 * kc) : u32x4{0u, 0u, 0u, 0u};
+      qf[kc] = __builtin_bit_cast(bf16x8, t);
+    }
+  }
+
+  const int key_stride_b = p.hkv * D * 2;
+  const char* kseq = (const char*)p.k + ((int64_t)si.k0 * p.hkv + g) * D * 2;
+  const char* vseq = (const char*)p.v + ((int64_t)si.k0 * p.hkv + g) * D * 2;
+  // K rows of a block in A-operand order: lane r32 holds key k_lds_row(r32)
+  const unsigned krow_off = (unsigned)(k_lds_row(r32) * key_stride_b + 16 * hf);
+  unsigned voff[VI];
+#pragma unroll
+  for (int u = 0; u < VI; ++u) {
+    const int P = u * 64 + lane;
+    const int row = P / CPR, pc = P % CPR;
+    voff[u] = (unsigned)(row * key_stride_b + ((pc ^ swz_v<D>(row)) * 16));
+  }
+  int va[DT];
+  {
+    const int tr_row = (lane & 15) >> 2;
+    const int lc_lo = ((lane >> 4) & 1) * 2 + ((lane & 3) >> 1);
+    const int half = (lane & 1) * 8;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int lc = 4 * t + lc_lo;
+      va[t] = (8 * hf + tr_row) * RB + ((lc ^ swz_v<D>(tr_row)) * 16) + half;
+    }
+  }
+
+  // Block i of this wave (key block j = wave + NWV*i): K into register slot
+  // i % NSTG, V into ring slot i % NSTG.  Keys at or past sk lie beyond the
+  // resources' num_records and arrive as zeros.
+  bf16x8 kreg[NSTG][KC];
+  // (device pass only: the host pass drops the kernel's launch stub when this
+  // lambda calls the buffer-load builtins)
+  auto issue = [&](const int i, bf16x8 (&kr)[KC]) __attribute__((always_inline)) {
+#if __HIP_DEVICE_COMPILE__
+    const int j = wave + NWV * i;
+    const int keys_left = si.sk - j * TK;  // > 0: j < nb
+    const char* kb = kseq + (int64_t)j * TK * key_stride_b;
+    const char* vb = vseq + (int64_t)j * TK * key_stride_b;
+    __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, keys_left * key_stride_b, kRsrcWord3);
+    __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, keys_left * key_stride_b, kRsrcWord3);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      kr[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rk, (int)(krow_off + 32 * kc), 0, 0));
+    char* dst = ring + __builtin_amdgcn_readfirstlane((i % NSTG) * VBUF);
+#pragma unroll
+    for (int u = 0; u < VI; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + u * 1024), 16, voff[u], 0,
+                                               0, 0);
+#endif
+  };
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    if (i < nmine) issue(i, kreg[i]);
+
+  // Blocks in groups of NSTG so that every slot index is a constant: block
+  // bb uses slot s = bb % NSTG; the slot of block bb + DEPTH is the one block
+  // bb - 1 released.
+  for (int i = 0; i < nmine; i += NSTG) {
+#pragma unroll
+    for (int s = 0; s < NSTG; ++s) {
+      const int bb = i + s;
+      if (bb >= nmine) break;
+      if (bb + DEPTH < nmine) issue(bb + DEPTH, kreg[(s + DEPTH) % NSTG]);
+      // Block bb's loads are complete once at most the blocks issued after
+      // it are outstanding (its V copy lands in LDS by the same count).  The
+      // asm keeps every memory access on its side of the wait.
+      const int newer = min(DEPTH, nmine - 1 - bb);
+      if (newer >= 3)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * BLK_LOADS) : "memory");
+      else if (newer == 2)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BLK_LOADS) : "memory");
+      else if (newer == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(BLK_LOADS) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const char* vslot = ring + s * VBUF;
+
+      // S^T = K Q^T: two accumulators over alternating k-chunks
+      f32x16 sa = f32x16{}, sb = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; kc += 2) {
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[s][kc], qf[kc], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[s][kc + 1], qf[kc + 1], sb, 0, 0, 0);
+      }
+      f32x16 sc = sa + sb;
+      // register r of half hf holds key j*TK + 16(r>>3) + 8hf + (r&7)
+      const int j = wave + NWV * bb;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j * TK + 16 * (r >> 3) + 8 * hf + (r & 7);
+        if (key > lim || !cvalid) sc[r] = -INFINITY;
+      }
+      float mx = fmax_nan(sc[0], sc[1]);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) mx = fmax_nan(fmax_nan(mx, sc[r]), sc[r + 1]);
+      const float m_new = fmax_nan(m_run, halfwave_max(mx));
+      if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy) != 0) {
+        const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      }
+      const float ms = (m_run == -INFINITY ? 0.f : m_run) * c;
+      bf16x8 pb[2];
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = exp2_fast(__builtin_fmaf(sc[r], c, -ms));
+        rs += pv;
+        pb[r >> 3][r & 7] = (__bf16)pv;
+      }
+      l_run += rs;
+      // O^T += V^T P^T over the block's two 16-key chunks
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2)
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vslot + 16 * kc2 * RB + va[t]));
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vslot + (16 * kc2 + 4) * RB + va[t]));
+          bf16x4 lob = __builtin_bit_cast(bf16x4, lo), hib = __builtin_bit_cast(bf16x4, hi);
+          bf16x8 a = {lob[0], lob[1], lob[2], lob[3], hib[0], hib[1], hib[2], hib[3]};
+          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], oacc[t], 0, 0, 0);
+        }
+    }
+  }
+
+  // ---- merge the four waves' partial states through LDS (the rings are free
+  // once every wave is past its loop)
+  pin_accumulators(oacc);
+  const float l_tot = halfwave_sum(l_run);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  char* const mine = smem + wave * (DT * 4096 + 512);
+#pragma unroll
+  for (int t = 0; t < DT; ++t) *(f32x16*)(mine + t * 4096 + lane * 64) = oacc[t];
+  *(float2*)(mine + DT * 4096 + lane * 8) = float2{m_run, l_tot};
+  __syncthreads();
+  float mw[NWV], lw[NWV];
+  float mmax = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const float2 ml = *(const float2*)(smem + w * (DT * 4096 + 512) + DT * 4096 + lane * 8);
+    mw[w] = ml.x;
+    lw[w] = ml.y;
+    mmax = fmax_nan(mmax, ml.x);
+  }
+  float wt[NWV], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    wt[w] = mmax == -INFINITY ? 0.f : exp2_fast((mw[w] - mmax) * c);
+    L += wt[w] * lw[w];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  __bf16* orow = (__bf16*)p.o + ((int64_t)(si.q0 + qrow) * p.hq + head) * D;
+  for (int t = wave; t < DT; t += NWV) {  // wave w finishes O^T tile w
+    f32x16 acc[1] = {f32x16{}};
+#pragma unroll
+    for (int w = 0; w < NWV; ++w)
+      acc[0] += wt[w] * *(const f32x16*)(smem + w * (DT * 4096 + 512) + t * 4096 + lane * 64);
+    store_o_rows<1>(acc, inv, orow + 32 * t, hf, cvalid);
+  }
+  if (wave == 0 && hf == 0 && cvalid)
+    p.lse[(int64_t)head * si.total_q + si.q0 + qrow] =
+        L > 0.f ? (mmax * c + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
 // FP8 (OCP e4m3) inputs.  Same tiling and pipeline as the bf16 kernel, on the
 // gfx950 fp8 MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (block scales fixed at
 // 2^0): each lane feeds 32 bytes of its row (A) or column (B); the 64 products
@@ -1155,6 +1399,11 @@ void launch_bf16_pp(const Launch& L, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 void launch_bf16(const Launch& L, hipStream_t stream) {
+  if (L.decode) {
+    hipLaunchKernelGGL((fa_fwd_bf16_decode_kernel<D, CAUSAL>), dim3((unsigned)L.num_workgroups),
+                       dim3(256), 0, stream, L.p);
+    return;
+  }
   if (L.pingpong) {
     launch_bf16_pp<D, CAUSAL>(L, stream);
     return;

@@ -12,6 +12,7 @@ constexpr int kTileN = 64;   // keys per main-loop step
 constexpr int kWaves = 4;    // wavefronts per workgroup
 constexpr int kStages = 2;   // K/V LDS buffers
 constexpr int kXcds = 8;     // XCDs of an MI355X; workgroups go round-robin over them
+constexpr int kDecodeSlots = 4;  // K register / V LDS slots per wave of the decode kernel
 
 // LDS per workgroup: K and V blocks of kTileN rows of d*2 bytes (no padding;
 // bank conflicts are avoided by swizzling 16-byte columns), double-buffered.
@@ -44,6 +45,7 @@ struct Launch {
   int fp8;
   int query_tiles;  // 32-row query tiles per wave (1 or 2)
   int pingpong;     // 1: the 8-wave ping-pong kernel (bf16, two query heads per workgroup)
+  int decode;       // 1: the decode kernel (bf16, a KV head's query rows in one tile)
   int64_t num_workgroups;
 };
 

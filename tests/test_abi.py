@@ -207,6 +207,18 @@ def test_plan_gfx950():
     # fp8 always uses schedule 1
     p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 32, 8, 16384, 16384, False, 128, 128, True)
     assert (p8.schedule, p8.tile_m, p8.query_tiles, p8.lds_bytes) == (1, 128, 1, 32 * KIB)
+    # decode: 4 query heads per KV head x 1 row fit one 32-column tile; one workgroup of 4
+    # waves per (sequence, kv-head), a 4-slot V ring of 32-key blocks per wave in LDS
+    pd = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 32, 32, 8, 1, 8192, False, 128, 128, True)
+    assert (pd.schedule, pd.tile_m, pd.tile_n, pd.waves, pd.kv_stages) == (4, 32, 32, 4, 4)
+    assert (pd.num_workgroups, pd.heads_per_workgroup, pd.wg_per_cu, pd.vgprs_per_lane) == \
+        (32 * 8, 4, 1, 512)
+    assert pd.lds_bytes == 4 * 4 * 32 * 128 * 2
+    # 8 heads x 4 rows = 32 columns still fits; 8 x 5 does not
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 4, 100, False, 64, 64, False).schedule == 4
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 5, 100, False, 64, 64, False).schedule == 3
+    # fp8 never takes it
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 32, 32, 8, 1, 8192, False, 128, 128, True).schedule == 1
 
 
 def test_schedule_override():
@@ -228,7 +240,12 @@ def test_schedule_override():
         # fp8 always uses 1
         p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 2, 1, 300, 300, False, 64, 64, False)
         assert p8.schedule == 1
-        for bad in (-1, 4):
+        # schedule 4 needs heads_q / heads_kv * seqlen_q <= 32: falls back to 1
+        fa.fa_set_schedule(4)
+        assert fa.fa_fwd_plan(*args).schedule == 1
+        assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 32, 8, 1, 8192, False, 128, 128,
+                              True).schedule == 4
+        for bad in (-1, 5):
             with pytest.raises(fa.FaError) as e:
                 fa.fa_set_schedule(bad)
             assert e.value.code == fa.FA_ERR_INVALID

@@ -11,10 +11,11 @@ from parity import compare, gather_rows, gpu_run, oracle_full, oracle_rows, samp
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=[1, 2, 3], ids=["sched1", "sched2", "sched3"])
+@pytest.fixture(params=[1, 2, 3, 4], ids=["sched1", "sched2", "sched3", "sched4"])
 def schedule(request):
     """Force each bf16 schedule (1: one query tile per wave; 2: two; 3: 8-wave ping-pong,
-    where heads_q / heads_kv is even, else 1) for the test."""
+    where heads_q / heads_kv is even; 4: decode, where heads_q / heads_kv * seqlen_q <= 32;
+    else 1) for the test."""
     import exact_attention_forward_fa_amd as fa
 
     fa.fa_set_schedule(request.param)
@@ -89,6 +90,8 @@ def test_varlen_equals_per_sequence_calls(schedule):
     o, lse = gpu_run(w)
     ro, rl = oracle_full(w)
     compare(o, lse, ro, rl, "bf16", w.name)
+    if schedule == 4:
+        return  # decode applies per call: the (1, 64) call takes it, the packed call cannot
     cu = w.cu_seqlens
     nb = len(lens)
     for b, (sq, sk) in enumerate(lens):
@@ -115,6 +118,35 @@ def test_ragged_shapes(shape, causal, d, schedule):
     b, hq, hkv, sq, sk = shape
     w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq * 7 + sk + d,
                        name=f"ragged_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}_c{int(causal)}_s{schedule}")
+    full_check(w)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 1, 1000), (1, 16, 4, 8, 777), (3, 16, 2, 4, 100),
+                                   (1, 4, 2, 16, 33), (2, 2, 2, 32, 5), (1, 8, 8, 1, 4096)])
+def test_decode_shapes(shape, causal, d):
+    """The decode schedule (all (head, row) pairs of a KV group in one 32-column tile, the key
+    range split over the waves) as the planner picks it: key counts that leave some waves with
+    no block or a partial one, causal rows that see few keys, groups of 1 to 8."""
+    import exact_attention_forward_fa_amd as fa
+
+    b, hq, hkv, sq, sk = shape
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, b, hq, hkv, sq, sk, False, d, d, causal).schedule == 4
+    w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq * 11 + sk + d,
+                       name=f"decode_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}_c{int(causal)}")
+    full_check(w)
+
+
+def test_decode_varlen():
+    """Varlen decode: per-sequence query rows 0 .. 4 (group 4 x 4 rows = 16 columns), key counts
+    from 0 to 3000, causal."""
+    import exact_attention_forward_fa_amd as fa
+
+    lens = [(1, 3000), (4, 37), (0, 500), (3, 0), (2, 1), (4, 2049)]
+    w = fa_inputs.make(0, 8, 2, 0, 0, 128, causal=True, seed=70, lengths=lens, name="decode_varlen")
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, len(lens), 8, 2, 4, 3000, True, 128, 128,
+                          True).schedule == 4
     full_check(w)
 
 
