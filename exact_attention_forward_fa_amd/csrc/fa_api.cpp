@@ -109,8 +109,8 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   //  * schedule 4 (bf16, heads_q / heads_kv * seqlen_q <= 32): decode -- all
   //    query rows of one KV head's group in the 32 columns of one tile, one
   //    workgroup per (sequence, KV head) whose 4 waves split the key range in
-  //    32-key blocks, each with a 4-slot K register / V LDS ring, 512
-  //    registers per lane (one wave per SIMD).
+  //    32-key blocks, each with a 2-slot K and V ring in LDS, one wave per
+  //    SIMD.
   // Automatic: 4 where it applies, else 3 where it applies, else 1.
   // fa_set_schedule forces one (falling back to 1 where it does not apply).
   const int64_t lds = fa::lds_bytes(head_dim, dtype == FA_DTYPE_E4M3 ? 1 : 2);
@@ -121,7 +121,7 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const bool bf16 = dtype == FA_DTYPE_BF16;
   const bool wide_ok = bf16 && L.regs_per_simd_lane >= 512;
   const bool pp_ok = bf16 && group % 2 == 0 && L.regs_per_simd_lane >= 512;
-  const int64_t decode_lds = 4LL * fa::kDecodeSlots * 32 * head_dim * 2;
+  const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&
                          L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;
   const int forced = g_schedule.load(std::memory_order_relaxed);

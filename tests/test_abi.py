@@ -208,12 +208,12 @@ def test_plan_gfx950():
     p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 32, 8, 16384, 16384, False, 128, 128, True)
     assert (p8.schedule, p8.tile_m, p8.query_tiles, p8.lds_bytes) == (1, 128, 1, 32 * KIB)
     # decode: 4 query heads per KV head x 1 row fit one 32-column tile; one workgroup of 4
-    # waves per (sequence, kv-head), a 4-slot V ring of 32-key blocks per wave in LDS
+    # waves per (sequence, kv-head), a 2-slot ring of 32-key K and V blocks per wave in LDS
     pd = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 32, 32, 8, 1, 8192, False, 128, 128, True)
-    assert (pd.schedule, pd.tile_m, pd.tile_n, pd.waves, pd.kv_stages) == (4, 32, 32, 4, 4)
+    assert (pd.schedule, pd.tile_m, pd.tile_n, pd.waves, pd.kv_stages) == (4, 32, 32, 4, 2)
     assert (pd.num_workgroups, pd.heads_per_workgroup, pd.wg_per_cu, pd.vgprs_per_lane) == \
         (32 * 8, 4, 1, 512)
-    assert pd.lds_bytes == 4 * 4 * 32 * 128 * 2
+    assert pd.lds_bytes == 4 * (2 * 2 * 32 * 128 * 2)
     # 8 heads x 4 rows = 32 columns still fits; 8 x 5 does not
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 4, 100, False, 64, 64, False).schedule == 4
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 5, 100, False, 64, 64, False).schedule == 3
