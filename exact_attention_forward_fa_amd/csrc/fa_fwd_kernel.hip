@@ -800,8 +800,10 @@ void fa_fwd_bf16_pp_kernel(Params p) {
                   char* __restrict__ kdst, char* __restrict__ vdst, auto qk_tag, auto pv_tag)
       __attribute__((always_inline)) {
     __syncthreads();
-    if (N - 2 - k >= 0) stage(kseq, koff, kdst, N - 2 - k);
-    if (N - 1 - k >= 0) stage(vseq, voff, vdst, N - 1 - k);
+    if (k >= 1) {  // step 0's loads are part of the prologue
+      if (N - 2 - k >= 0) stage(kseq, koff, kdst, N - 2 - k);
+      if (N - 1 - k >= 0) stage(vseq, voff, vdst, N - 1 - k);
+    }
     if (grp == 0) {
       gemm(kread, vread, qk_tag, pv_tag);
     } else if (k >= 1) {
@@ -823,7 +825,12 @@ void fa_fwd_bf16_pp_kernel(Params p) {
     vd = vbuf0 + par * BUF;
   };
 
-  stage(kseq, koff, kbuf0, N - 1);  // K_{N-1}: buffer 0
+  // the prologue loads what steps 0 and 1 read: K_{N-1} (buffer 0), K_{N-2}
+  // (buffer 1) and V_{N-1} (V buffer 0), so the short step 0 leaves no load
+  // in flight for step 1's barrier to wait out
+  stage(kseq, koff, kbuf0, N - 1);
+  if (N >= 2) stage(kseq, koff, kbuf0 + BUF, N - 2);
+  stage(vseq, voff, vbuf0, N - 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   {
     const char *kr, *vr;
