@@ -230,6 +230,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--exp2-offload", type=int, default=0, choices=[0, 4, 8],
+                    help="ping-pong schedule: every N-th exponential on the FMA polynomial "
+                         "(0: off, the default)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES bytes (counter scaling) and exit")
     args = ap.parse_args(argv)
@@ -255,6 +258,7 @@ def main(argv=None) -> int:
     if args.workload in KVCACHE_WORKLOADS:
         return run_kvcache(args, KVCACHE_WORKLOADS[args.workload])
     w = fa_inputs.workload(args.workload)
+    fa.fa_set_exp2_offload(args.exp2_offload)
     log(f"workload {w.name}: batch={w.batch} hq={w.heads_q} hkv={w.heads_kv} sq={w.seqlen_q} "
         f"sk={w.seqlen_k} d={w.head_dim} causal={w.causal} dtype={w.dtype}")
     q, k, v = w.q.cuda(), w.k.cuda(), w.v.cuda()
@@ -315,9 +319,12 @@ def main(argv=None) -> int:
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": load_traffic(w.name), "kernel_ms": round(kernel_ms, 5)},
+                     "traffic": None if args.exp2_offload else load_traffic(w.name),
+                     "kernel_ms": round(kernel_ms, 5)},
         "cpu_baseline": cpu,
     }
+    if args.exp2_offload:
+        line["config"]["exp2_offload"] = args.exp2_offload
     print(json.dumps(line), flush=True)
     return 0
 

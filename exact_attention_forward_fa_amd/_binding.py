@@ -84,6 +84,8 @@ def _load():
     lib.fa_version.restype = i32
     lib.fa_set_schedule.argtypes = [i32]
     lib.fa_set_schedule.restype = i32
+    lib.fa_set_exp2_offload.argtypes = [i32]
+    lib.fa_set_exp2_offload.restype = i32
     lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                    i32, i32, ctypes.c_float, i32, vp, vp]
     lib.fa_fwd_kvcache.restype = i32
@@ -108,6 +110,14 @@ def fa_set_schedule(schedule: int) -> None:
     rc = _lib.fa_set_schedule(int(schedule))
     if rc != 0:
         raise FaError(rc, "fa_set_schedule")
+
+
+def fa_set_exp2_offload(every: int) -> None:
+    """exp2 offload in the ping-pong schedule: 0 off (default), or every 4th / 8th exponential
+    on the FMA polynomial instead of the transcendental unit."""
+    rc = _lib.fa_set_exp2_offload(int(every))
+    if rc != 0:
+        raise FaError(rc, "fa_set_exp2_offload")
 
 
 def fa_gfx950_limits() -> DeviceLimits:

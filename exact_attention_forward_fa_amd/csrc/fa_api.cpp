@@ -18,6 +18,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 // fa_set_schedule: 0 automatic, else the forced schedule (1 .. 4)
 std::atomic<int> g_schedule{0};
+// fa_set_exp2_offload: 0, 4 or 8
+std::atomic<int> g_exp2_offload{0};
 
 // gfx950 (MI355X): 160 KiB LDS per CU, all of it addressable by one
 // workgroup; 256 CUs; 4 SIMDs per CU; 512 VGPR+AGPR per lane per SIMD;
@@ -53,6 +55,12 @@ const char* fa_strerror(int code) {
 int fa_set_schedule(int schedule) {
   if (schedule < 0 || schedule > 4) return FA_ERR_INVALID;
   g_schedule.store(schedule, std::memory_order_relaxed);
+  return FA_OK;
+}
+
+int fa_set_exp2_offload(int every) {
+  if (every != 0 && every != 4 && every != 8) return FA_ERR_INVALID;
+  g_exp2_offload.store(every, std::memory_order_relaxed);
   return FA_OK;
 }
 
@@ -229,6 +237,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   L.query_tiles = qt;
   L.pingpong = plan.schedule == 3;
   L.decode = plan.schedule == 4;
+  L.exp2_offload = L.pingpong ? g_exp2_offload.load(std::memory_order_relaxed) : 0;
   return fa::launch(L, stream);
 }
 

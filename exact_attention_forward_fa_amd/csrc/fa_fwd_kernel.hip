@@ -42,6 +42,24 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x on the FMA pipe instead of the transcendental unit -- the polynomial
+// replacement of the exponential that "Dissecting the SM_120
+// Microarchitecture" lists first among the remedies for the softmax-bound
+// FlashAttention tile (section 11.2, Fig. 12).  Cody-Waite split x = n + f
+// with n = rint(x), f in [-1/2, 1/2]; 2^f by a degree-3 polynomial fitted here
+// by iterated weighted least squares for relative error on [-1/2, 1/2] (max
+// 7.5e-5, below the bf16 rounding of P); 2^n by ldexp.  x is clamped at -160,
+// so a masked score (-inf) gives exactly 0; NaN propagates.
+__device__ __forceinline__ float exp2_poly(float x) {
+  x = __builtin_elementwise_maximum(x, -160.f);
+  const float n = __builtin_rintf(x);
+  const float f = x - n;
+  float p = __builtin_fmaf(0.05517605319619179f, f, 0.24261149764060974f);
+  p = __builtin_fmaf(p, f, 0.6932601928710938f);
+  p = __builtin_fmaf(p, f, 0.9999280571937561f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
 // Maximum that propagates NaN (IEEE 754-2019 maximum).  Scores are never NaN
 // here; unlike fmaxf it needs no quieting of its inputs, and chains of it map
 // onto v_maximum3_f32.
@@ -587,7 +605,7 @@ void fa_fwd_bf16_kernel(Params p) {
 #ifndef PP_AHEAD
 #define PP_AHEAD 20
 #endif
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int XQ>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_pp_kernel(Params p) {
   constexpr int TM = kTileM, TN = kTileN;
@@ -744,7 +762,9 @@ void fa_fwd_bf16_pp_kernel(Params p) {
 #pragma unroll
     for (int idx = 0; idx < 32; ++idx) {
       const int tt = idx >> 4, r = idx & 15;
-      const float pv = exp2_fast(__builtin_fmaf(sc[tt][r], c, -ms));
+      // XQ > 0: every XQ-th exponential on the FMA polynomial (exp2 offload)
+      const float x = __builtin_fmaf(sc[tt][r], c, -ms);
+      const float pv = (XQ > 0 && idx % XQ == XQ - 1) ? exp2_poly(x) : exp2_fast(x);
       rs += pv;
       pb[2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
     }
@@ -799,6 +819,11 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   auto step = [&](const int k, const char* __restrict__ kread, const char* __restrict__ vread,
                   char* __restrict__ kdst, char* __restrict__ vdst, auto qk_tag, auto pv_tag)
       __attribute__((always_inline)) {
+    // Each wave's own direct-to-LDS loads must be complete before the barrier
+    // for the other waves to read them.  The wait is written out: the
+    // barrier's fence does not oblige the compiler to wait for loads, and in
+    // some code shapes it does not.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (k >= 1) {  // step 0's loads are part of the prologue
       if (N - 2 - k >= 0) stage(kseq, koff, kdst, N - 2 - k);
@@ -1409,8 +1434,13 @@ void launch_fp8(const Launch& L, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 void launch_bf16_pp(const Launch& L, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_bf16_pp_kernel<D, CAUSAL>), dim3((unsigned)L.num_workgroups),
-                     dim3(512), 0, stream, L.p);
+  const dim3 grid((unsigned)L.num_workgroups), block(512);
+  if (L.exp2_offload == 4)
+    hipLaunchKernelGGL((fa_fwd_bf16_pp_kernel<D, CAUSAL, 4>), grid, block, 0, stream, L.p);
+  else if (L.exp2_offload == 8)
+    hipLaunchKernelGGL((fa_fwd_bf16_pp_kernel<D, CAUSAL, 8>), grid, block, 0, stream, L.p);
+  else
+    hipLaunchKernelGGL((fa_fwd_bf16_pp_kernel<D, CAUSAL, 0>), grid, block, 0, stream, L.p);
 }
 
 template <int D, bool CAUSAL>

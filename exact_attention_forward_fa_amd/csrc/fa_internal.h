@@ -46,6 +46,7 @@ struct Launch {
   int query_tiles;  // 32-row query tiles per wave (1 or 2)
   int pingpong;     // 1: the 8-wave ping-pong kernel (bf16, two query heads per workgroup)
   int decode;       // 1: the decode kernel (bf16, a KV head's query rows in one tile)
+  int exp2_offload; // ping-pong only: 0, or every 4th / 8th exponential on the FMA polynomial
   int64_t num_workgroups;
 };
 

@@ -203,9 +203,13 @@ typedef struct fa_plan {
  *      feeding two matrix instructions;
  *   3  bf16, heads_q / heads_kv even: 8 waves in two groups of four, 128 rows
  *      of two query heads that share a KV head (one K/V staging for both),
- *      the groups alternating matrix-core and softmax phases (ping-pong).
- * The plan uses 3 where it applies, else 1, unless fa_set_schedule forces
- * one.
+ *      the groups alternating matrix-core and softmax phases (ping-pong);
+ *   4  bf16, heads_q / heads_kv * seqlen_q <= 32 (decode): the (query head,
+ *      row) pairs of one KV head in the 32 columns of one tile, one workgroup
+ *      per (sequence, KV head) whose 4 waves split the key range and merge
+ *      their partial softmax states at the end.
+ * The plan uses 4 where it applies, else 3 where it applies, else 1, unless
+ * fa_set_schedule forces one.
  */
 int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
                 int varlen, int head_dim, int head_dim_v, int causal,
@@ -214,7 +218,7 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
 /*
  * fa_set_schedule -- tuning override of the planner's schedule choice (for
  * benchmarking and for tests that run every schedule on the same shapes).
- * 0 restores the automatic choice; 1, 2 or 3 forces that schedule in every
+ * 0 restores the automatic choice; 1, 2, 3 or 4 forces that schedule in every
  * later fa_fwd / fa_fwd_kvcache / fa_fwd_plan call of the process wherever it
  * applies (schedule 1 elsewhere).  All schedules compute the same function to
  * within rounding, but not bit for bit: the reference maximum that the
@@ -224,6 +228,20 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
  * value.
  */
 int fa_set_schedule(int schedule);
+
+/*
+ * fa_set_exp2_offload -- exp2 offload ("Dissecting the SM_120
+ * Microarchitecture", section 11.2, Fig. 12, first remedy for the
+ * softmax-bound tile): in the ping-pong schedule (3), evaluate every 4th or
+ * 8th exponential of P with a Cody-Waite reduction and a degree-3 polynomial
+ * on the FMA pipe instead of the transcendental unit (relative error below
+ * 7.5e-5, under the bf16 rounding of P).  0 (the default) turns it off.  On
+ * gfx950 it measures slower (the vector ALU, not the transcendental unit, is
+ * the contended resource), so it is a tuning and study switch.  Process-wide
+ * atomic like fa_set_schedule.  Returns FA_OK, or FA_ERR_INVALID for values
+ * other than 0, 4 and 8.
+ */
+int fa_set_exp2_offload(int every);
 
 /* Library version: major*10000 + minor*100 + patch. */
 int fa_version(void);

@@ -254,6 +254,18 @@ def test_schedule_override():
     assert fa.fa_fwd_plan(*args).schedule == 3
 
 
+def test_exp2_offload_setting():
+    try:
+        for ok in (4, 8, 0):
+            fa.fa_set_exp2_offload(ok)
+        for bad in (-1, 1, 2, 3, 5, 16):
+            with pytest.raises(fa.FaError) as e:
+                fa.fa_set_exp2_offload(bad)
+            assert e.value.code == fa.FA_ERR_INVALID
+    finally:
+        fa.fa_set_exp2_offload(0)
+
+
 def test_plan_reports_unsupported_when_nothing_fits():
     small = fa.DeviceLimits(lds_bytes_per_block=48 * KIB, lds_bytes_per_cu=48 * KIB, num_cus=1,
                             simds_per_cu=4, regs_per_simd_lane=512, max_waves_per_simd=8)

@@ -150,6 +150,66 @@ def test_decode_varlen():
     full_check(w)
 
 
+@pytest.mark.parametrize("every", [4, 8])
+@pytest.mark.parametrize("shape", [(2, 4, 2, 300, 300, 128, True), (1, 8, 2, 200, 517, 64, False),
+                                   (1, 4, 2, 517, 200, 128, True)])
+def test_exp2_offload(shape, every):
+    """Ping-pong schedule with every 4th / 8th exponential on the FMA polynomial: same
+    tolerances against the oracle."""
+    import exact_attention_forward_fa_amd as fa
+
+    b, hq, hkv, sq, sk, d, causal = shape
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, b, hq, hkv, sq, sk, False, d, d, causal).schedule == 3
+    w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq + sk + every,
+                       name=f"exp2_offload{every}_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}")
+    fa.fa_set_exp2_offload(every)
+    try:
+        full_check(w)
+    finally:
+        fa.fa_set_exp2_offload(0)
+
+
+def test_exp2_offload_large_q():
+    """Peaked softmax rows (Q x 50): the polynomial's relative error must not show in LSE."""
+    import exact_attention_forward_fa_amd as fa
+
+    w = fa_inputs.make(1, 4, 2, 256, 256, 128, causal=True, seed=65, q_mult=50.0,
+                       name="exp2_offload_q_x50")
+    fa.fa_set_exp2_offload(4)
+    try:
+        full_check(w)
+    finally:
+        fa.fa_set_exp2_offload(0)
+
+
+@pytest.mark.parametrize("shape", [(8, 8, 2, 1, 4096), (4, 16, 4, 3, 2500)])
+def test_pingpong_short_steps_repeat(shape):
+    """The ping-pong schedule on shapes whose steps are short (one or a few query rows, many
+    key blocks): each step's K/V loads must be complete before the next step's barrier, or
+    waves read half-written blocks.  Five calls, each against the oracle and all bit-identical."""
+    import exact_attention_forward_fa_amd as fa
+
+    b, hq, hkv, sq, sk = shape
+    w = fa_inputs.make(b, hq, hkv, sq, sk, 128, causal=True, seed=sq + sk,
+                       name=f"pp_short_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}")
+    fa.fa_set_schedule(3)
+    try:
+        assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, b, hq, hkv, sq, sk, False, 128, 128,
+                              True).schedule == 3
+        t = to_device(w)
+        ro, rl = oracle_full(w)
+        first = None
+        for rep in range(5):
+            o, lse = gpu_run(w, t)
+            compare(o, lse, ro, rl, "bf16", f"{w.name}_rep{rep}")
+            if first is None:
+                first = (o, lse)
+            else:
+                assert np.array_equal(o, first[0]) and np.array_equal(lse, first[1])
+    finally:
+        fa.fa_set_schedule(0)
+
+
 def test_seqlen_k_zero():
     w = fa_inputs.make(2, 2, 2, 100, 0, 128, causal=False, seed=60, name="sk0")
     o, lse = gpu_run(w)
