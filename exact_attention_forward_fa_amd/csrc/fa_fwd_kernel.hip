@@ -1,9 +1,18 @@
 // fa_fwd_kernel.hip -- exact attention forward for gfx950 (MI355X, CDNA4).
 //
-// One workgroup = 4 wavefronts = 128 query rows of one (sequence, head).
-// Each wave owns 32 query rows and walks the key blocks (64 keys each) from
-// the last admissible block down to the first, the block order of the
-// consumer loop in "FlashAttention core algorithm: forward pass".
+// Four schedules of one computation (the planner in fa_api.cpp picks one):
+//  1. fa_fwd_bf16_kernel<.., QG = 1> / fa_fwd_fp8_kernel: 4 waves = 128 query
+//     rows of one (sequence, head), two workgroups per CU;
+//  2. fa_fwd_bf16_kernel<.., QG = 2>: 256 rows, one wave per SIMD;
+//  3. fa_fwd_bf16_pp_kernel: 8 waves, two query heads of one KV head, the
+//     two groups of waves alternating GEMM and softmax phases (ping-pong);
+//  4. fa_fwd_bf16_decode_kernel: a KV head's (query head, row) pairs in one
+//     32-column tile, the 4 waves splitting the key range.
+// The description below is that of schedule 1; the others say how they
+// differ.  One workgroup = 4 wavefronts = 128 query rows of one (sequence,
+// head).  Each wave owns 32 query rows and walks the key blocks (64 keys
+// each) from the last admissible block down to the first, the block order of
+// the consumer loop in "FlashAttention core algorithm: forward pass".
 //
 // Per key block n the wave computes, on the matrix cores, the transposed
 // score tile S^T = K_n Q^T (v_mfma_f32_32x32x16_bf16, fp32 accumulate), so
@@ -17,8 +26,9 @@
 // the operand order the second product expects.  V stays row-major in LDS
 // and is read transposed with ds_read_b64_tr_b16.
 //
-// K/V blocks are double-buffered in LDS and prefetched one block ahead into
-// registers, so one barrier per block suffices.  The epilogue normalises by
+// K/V blocks are double-buffered in LDS and loaded one block ahead by
+// buffer loads that write LDS directly, so one barrier per block suffices
+// (each wave waits for its own loads before it).  The epilogue normalises by
 // the row sum, writes O (bf16) and LSE (fp32, natural log), and writes
 // O = 0 / LSE = -inf for rows with no admissible key -- the store_zero path
 // of the page's epilogue.
@@ -600,8 +610,10 @@ void fa_fwd_bf16_kernel(Params p) {
 //   slot 2k+1: A: softmax of N-1-k   B: GEMM(k)
 // GEMM(k) = S <- K_{N-1-k} Q^T (k < N) and O += V_{N-k}^T P^T (k >= 1).  K_j
 // lives in K buffer (N-1-j) & 1 and V_j in V buffer (N-1-j) & 1; at the start
-// of slot 2k all eight waves load K_{N-2-k} and V_{N-1-k}, two slots before
-// their first use, into the buffers whose last readers finished in slot 2k-1.
+// of slot 2k (k >= 1) all eight waves load K_{N-2-k} and V_{N-1-k}, two slots
+// before their first use, into the buffers whose last readers finished in
+// slot 2k-1; the prologue loads step 0's share (K_{N-1}, K_{N-2}, V_{N-1}).
+// XQ > 0 puts every XQ-th exponential on the FMA polynomial (exp2 offload).
 #ifndef PP_AHEAD
 #define PP_AHEAD 20
 #endif
