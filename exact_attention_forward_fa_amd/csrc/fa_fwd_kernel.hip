@@ -603,9 +603,10 @@ void fa_fwd_bf16_kernel(Params p) {
 // between a GEMM slot -- the QK^T of the next block and the P V of the current
 // one, with all their LDS operand reads -- and a softmax slot (VALU and the
 // transcendental unit only), offset by one slot: while one wave of a SIMD
-// keeps the matrix core busy, the other exponentiates.  Slots are separated
-// by workgroup barriers.  Step k (k = 0 .. N, N key blocks, block N-1-k is
-// the one whose scores step k computes):
+// keeps the matrix core busy, the other exponentiates.  Each step starts at
+// a workgroup barrier; within it the groups run their two phases back to back
+// in opposite order.  Step k (k = 0 .. N, N key blocks, block N-1-k is the
+// one whose scores step k computes):
 //   slot 2k:   A: GEMM(k)            B: softmax of block N-k (k >= 1)
 //   slot 2k+1: A: softmax of N-1-k   B: GEMM(k)
 // GEMM(k) = S <- K_{N-1-k} Q^T (k < N) and O += V_{N-k}^T P^T (k >= 1).  K_j
@@ -841,16 +842,24 @@ void fa_fwd_bf16_pp_kernel(Params p) {
       if (N - 2 - k >= 0) stage(kseq, koff, kdst, N - 2 - k);
       if (N - 1 - k >= 0) stage(vseq, voff, vdst, N - 1 - k);
     }
+    // The two phases follow each other without a barrier (one between them
+    // would publish nothing): the step's full barrier starts the groups in
+    // opposite phases, a group that finishes its first phase early starts its
+    // second at once, and the GEMM phase runs at raised wave priority so that
+    // the SIMD's other wave, in its softmax phase, yields the issue slots the
+    // matrix instructions and their LDS reads need.  The s_setprio
+    // instructions also keep the compiler from mixing the two phases' code.
+    // Measured 1.6 % faster than a barrier between the phases.
     if (grp == 0) {
+      __builtin_amdgcn_s_setprio(1);
       gemm(kread, vread, qk_tag, pv_tag);
-    } else if (k >= 1) {
-      softmax(N - k);
-    }
-    asm volatile("s_barrier" ::: "memory");
-    if (grp == 0) {
+      __builtin_amdgcn_s_setprio(0);
       if (k < N) softmax(N - 1 - k);
     } else {
+      if (k >= 1) softmax(N - k);
+      __builtin_amdgcn_s_setprio(1);
       gemm(kread, vread, qk_tag, pv_tag);
+      __builtin_amdgcn_s_setprio(0);
     }
   };
   auto bufs = [&](const int k, const char*& kr, const char*& vr, char*& kd, char*& vd)
