@@ -342,6 +342,22 @@ def test_kvcache_prefill_chunk(causal, d, schedule):
     kvcache_check(case, f"kv_chunk_d{d}_c{int(causal)}_s{schedule}")
 
 
+def test_kvcache_decode_bench_workload():
+    """The KV-cache decode step bench.py times, at full size (32 sequences, 8192-row caches,
+    32 query / 8 KV heads), in the configuration it times (the planner's decode schedule):
+    caches bit for bit, every output row against the oracle."""
+    import bench
+    import exact_attention_forward_fa_amd as fa
+
+    name = "kvcache_decode_b32_hq32_hkv8_c8192_d128"
+    cfg = bench.KVCACHE_WORKLOADS[name]
+    b, hq, hkv, cap, d = cfg["batch"], cfg["heads_q"], cfg["heads_kv"], cfg["capacity"], cfg["head_dim"]
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, b, hq, hkv, 1, cap, False, d, d, True).schedule == 4
+    case = fa_inputs.make_kvcache(b, 1, 1, cap, [cap - 1] * b, hq, hkv, d, causal=True,
+                                  seed=cfg["seed"])
+    kvcache_check(case, name)
+
+
 def test_kvcache_no_new_rows():
     case = fa_inputs.make_kvcache(3, 17, 0, 512, [0, 200, 512], 4, 1, 128, causal=True, seed=84)
     kvcache_check(case, "kv_no_new_rows")
