@@ -133,10 +133,11 @@ __device__ __forceinline__ SeqInfo seq_info(const Params& p, int b) {
   return s;
 }
 
-// A row max may grow by up to 2^kLazy (in exp2 units) before O and l are
-// rescaled: P then stays <= 2^kLazy, and O / l is unchanged because both are
-// taken relative to the same stale maximum.
+// A row max may grow by up to kLazy (in exp2 units) before O and l are
+// rescaled: P then stays <= 2^kLazy = kLazyBound, and O / l is unchanged
+// because both are taken relative to the same stale maximum.
 constexpr float kLazy = 8.f;
+constexpr float kLazyBound = 256.f;
 
 // Instruction classes of the scheduling hints (LLVM AMDGPU sched_group_barrier
 // masks); the hints only order instructions the compiler already emits.
@@ -466,45 +467,29 @@ void fa_fwd_bf16_kernel(Params p) {
       }
     }
 
-    // block row max (in-lane, then across the two half-waves); lazy rescale
-    // only when some row's max grew by more than 2^kLazy (m_run = -inf and a
-    // finite m_new gives +inf > kLazy; both -inf give NaN)
-    float m_new[QG];
-    bool grow = false;
-#pragma unroll
-    for (int q = 0; q < QG; ++q) {
-      m_new[q] = fmax_nan(m_run[q], halfwave_max(block_max(sc[q])));
-      grow = grow || (m_new[q] - m_run[q]) * c > kLazy;
-    }
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
-      // With QG = 2 the O accumulators live in AGPRs and the scaling below
-      // needs VGPR copies; redefining them here keeps the compiler from
-      // hoisting those copies out of this rarely taken branch.
-      if constexpr (QG == 2) {
-#pragma unroll
-        for (int q = 0; q < QG; ++q) pin_accumulators_agpr(oacc[q]);
-      }
-#pragma unroll
-      for (int q = 0; q < QG; ++q) {
-        // 0 when m_run = -inf < m_new; rows whose max is still -inf hold O = 0
-        // and l = 0 and keep them (their alpha would be exp2(NaN))
-        const float alpha = m_new[q] == -INFINITY ? 1.f : exp2_fast((m_run[q] - m_new[q]) * c);
-        m_run[q] = m_new[q];
-        l_run[q] *= alpha;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) oacc[q][t] *= alpha;
-      }
-    }
-    float ms[QG];
-#pragma unroll
-    for (int q = 0; q < QG; ++q) ms[q] = (m_run[q] == -INFINITY ? 0.f : m_run[q]) * c;
-
-    // P = exp2(c*S - c*m), row sum, bf16 B operands -- interleaved with the
-    // MFMAs of the next block's scores
+    // P = exp2(c*S - c*m) against the running maximum, row sum, bf16 B
+    // operands -- interleaved with the MFMAs of the next block's scores.  No
+    // block maximum is taken first: the pass stands when every lane's share
+    // of each row sum is at most kLazyBound (then no P exceeds the bound the
+    // lazy rescale keeps); otherwise -- a maximum that grew, or a row with no
+    // maximum yet, whose P are inf or NaN -- the block maximum is taken (in
+    // lane, then across the two half-waves), O and l are rescaled to it where
+    // it grew, and P is computed again.
     float rs[QG];
     bf16x8 pb[QG][4];
+    auto expo = [&](const float (&ms)[QG], const int idx) __attribute__((always_inline)) {
+      const int tt = idx >> 4, r = idx & 15;
+#pragma unroll
+      for (int q = 0; q < QG; ++q) {
+        const float pv = exp2_fast(__builtin_fmaf(sc[q][tt][r], c, -ms[q]));
+        rs[q] += pv;
+        pb[q][2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
+      }
+    };
+    float ms[QG];
 #pragma unroll
     for (int q = 0; q < QG; ++q) {
+      ms[q] = m_run[q] * c;
       rs[q] = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t) sn[q][t] = f32x16{};
@@ -518,16 +503,46 @@ void fa_fwd_bf16_kernel(Params p) {
         for (int q = 0; q < QG; ++q)
           sn[q][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[q][kc], sn[q][t], 0, 0, 0);
       }
+      expo(ms, 2 * step);  // two of this lane's 32 scores per step and group
+      expo(ms, 2 * step + 1);
+    }
+    bool redo = false;
 #pragma unroll
-      for (int q = 0; q < QG; ++q)
+    for (int q = 0; q < QG; ++q) redo = redo || !(rs[q] <= kLazyBound);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(redo) != 0, 0)) {
+      float m_new[QG];
+      bool grow = false;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {  // two of this lane's 32 scores per step and group
-          const int idx = 2 * step + e;
-          const int tt = idx >> 4, r = idx & 15;
-          const float pv = exp2_fast(__builtin_fmaf(sc[q][tt][r], c, -ms[q]));
-          rs[q] += pv;
-          pb[q][2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
+      for (int q = 0; q < QG; ++q) {
+        m_new[q] = fmax_nan(m_run[q], halfwave_max(block_max(sc[q])));
+        grow = grow || m_new[q] > m_run[q];
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        // With QG = 2 the O accumulators live in AGPRs and the scaling below
+        // needs VGPR copies; redefining them here keeps the compiler from
+        // hoisting those copies out of this rarely taken branch.
+        if constexpr (QG == 2) {
+#pragma unroll
+          for (int q = 0; q < QG; ++q) pin_accumulators_agpr(oacc[q]);
         }
+#pragma unroll
+        for (int q = 0; q < QG; ++q) {
+          // 0 when m_run = -inf < m_new; rows whose max is still -inf hold O =
+          // 0 and l = 0 and keep them (their alpha would be exp2(NaN))
+          const float alpha = m_new[q] == -INFINITY ? 1.f : exp2_fast((m_run[q] - m_new[q]) * c);
+          m_run[q] = m_new[q];
+          l_run[q] *= alpha;
+#pragma unroll
+          for (int t = 0; t < DT; ++t) oacc[q][t] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < QG; ++q) {
+        ms[q] = (m_run[q] == -INFINITY ? 0.f : m_run[q]) * c;
+        rs[q] = 0.f;
+      }
+#pragma unroll
+      for (int idx = 0; idx < 32; ++idx) expo(ms, idx);
     }
 #pragma unroll
     for (int q = 0; q < QG; ++q) l_run[q] += rs[q];
@@ -762,24 +777,37 @@ void fa_fwd_bf16_pp_kernel(Params p) {
           if (key > lim) sc[t][r] = -INFINITY;
         }
     }
-    const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy) != 0, 0)) {
-      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
-      m_run = m_new;
-      l_run *= alpha;
+    // P is first taken against the running maximum without the block's own
+    // maximum.  The pass stands when every lane's share of the row sum is at
+    // most kLazyBound: then no P exceeds it, the bound the lazy rescale keeps.
+    // Otherwise (a maximum that grew, a row with no maximum yet: its P are
+    // inf or NaN) the block maximum is taken, O and l are rescaled to it if
+    // it grew, and P is computed again.  Saves the max reduction (a sixth of
+    // the softmax's instructions) on nearly every block.
+    auto expo = [&](const float ms) __attribute__((always_inline)) {
+      float rs = 0.f;
 #pragma unroll
-      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
-    }
-    const float ms = (m_run == -INFINITY ? 0.f : m_run) * c;
-    float rs = 0.f;
+      for (int idx = 0; idx < 32; ++idx) {
+        const int tt = idx >> 4, r = idx & 15;
+        // XQ > 0: every XQ-th exponential on the FMA polynomial (exp2 offload)
+        const float x = __builtin_fmaf(sc[tt][r], c, -ms);
+        const float pv = (XQ > 0 && idx % XQ == XQ - 1) ? exp2_poly(x) : exp2_fast(x);
+        rs += pv;
+        pb[2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
+      }
+      return rs;
+    };
+    float rs = expo(m_run * c);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= kLazyBound)) != 0, 0)) {
+      const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-    for (int idx = 0; idx < 32; ++idx) {
-      const int tt = idx >> 4, r = idx & 15;
-      // XQ > 0: every XQ-th exponential on the FMA polynomial (exp2 offload)
-      const float x = __builtin_fmaf(sc[tt][r], c, -ms);
-      const float pv = (XQ > 0 && idx % XQ == XQ - 1) ? exp2_poly(x) : exp2_fast(x);
-      rs += pv;
-      pb[2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
+        for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      }
+      rs = expo((m_run == -INFINITY ? 0.f : m_run) * c);
     }
     l_run += rs;
   };
@@ -1367,28 +1395,17 @@ void fa_fwd_fp8_kernel(Params p) {
           if (n * TN + 32 * hf + 16 * t + r > lim) sc[t][r] = -INFINITY;
     }
 
-    const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kLazy) != 0, 0)) {
-      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
-    }
-    const float ms = (m_run == -INFINITY ? 0.f : m_run) * c;
-
     // P = exp2(c*S - c*m) -> e4m3 bytes 16t + r of this half's B operand,
-    // under the MFMAs of the next block's scores
+    // under the MFMAs of the next block's scores, against the running maximum
+    // without the block's own: the pass stands when every lane's share of
+    // the row sum is at most kLazyBound (so every P is within the bound the
+    // lazy rescale keeps, below e4m3's largest value); otherwise -- a maximum
+    // that grew, a row with no maximum yet -- the block maximum is taken, O
+    // and l are rescaled to it where it grew, and P is computed again.
     float rs = 0.f;
     i32x8 pb;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) sn[t] = f32x16{};
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {  // dword w of P: bytes 4w .. 4w+3
-      if ((w & 1) == 0 && (w >> 1) < 2 * KC) {
-        const int i = w >> 1, kc = i >> 1, t = i & 1;
-        sn[t] = mfma_fp8(k_operand(kread, t, kc), qf[kc], sn[t]);
-      }
+    auto pword = [&](const float ms, const int w) __attribute__((always_inline)) {
+      // dword w of P: bytes 4w .. 4w+3
       const int t = w >> 2, r0 = 4 * (w & 3);
       float pv[4];
 #pragma unroll
@@ -1399,6 +1416,30 @@ void fa_fwd_fp8_kernel(Params p) {
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
       pb[w] = word;
+    };
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sn[t] = f32x16{};
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      if ((w & 1) == 0 && (w >> 1) < 2 * KC) {
+        const int i = w >> 1, kc = i >> 1, t = i & 1;
+        sn[t] = mfma_fp8(k_operand(kread, t, kc), qf[kc], sn[t]);
+      }
+      pword(m_run * c, w);
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= kLazyBound)) != 0, 0)) {
+      const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      }
+      const float ms = (m_run == -INFINITY ? 0.f : m_run) * c;
+      rs = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) pword(ms, w);
     }
     l_run += rs;
 

@@ -15,6 +15,12 @@ Recipe (every workload):
   * variable-length batches draw their lengths from
     ``numpy.random.default_rng(seed)`` and pack sequences back to back;
     ``cu_seqlens`` is int32[2*(batch+1)]: query offsets, then key offsets.
+  * ``key_offsets`` (optional, one float per key position): dimension 0 of
+    every query is set to 1 and dimension 0 of key j to
+    key_offsets[j] / (softmax_scale * log2 e), before rounding or
+    quantising, so every query's scaled score with key j gains about
+    key_offsets[j] in base-2 units on top of the random part of the other
+    dimensions: a controlled shape of the running row maximum.
   * KV-cache cases draw q, k_cache, v_cache, k_new, v_new in that order; the
     whole cache is filled (rows past the used length too); fp8 quantises the
     cache and the new rows of K (and of V) with one shared descale.
@@ -87,8 +93,10 @@ def _quant_e4m3(x: torch.Tensor) -> Tuple[torch.Tensor, float]:
 def make(batch: int, heads_q: int, heads_kv: int, seqlen_q: int, seqlen_k: int, head_dim: int,
          head_dim_v: Optional[int] = None, *, causal: bool, seed: int, dtype: str = "bf16",
          lengths: Optional[Sequence[Tuple[int, int]]] = None, softmax_scale: Optional[float] = None,
-         q_mult: float = 1.0, fp8_mult: float = 0.5, name: str = "custom") -> Workload:
-    """Build one workload.  ``lengths`` (list of (sq, sk)) makes a packed varlen batch."""
+         q_mult: float = 1.0, fp8_mult: float = 0.5, key_offsets: Optional[Sequence[float]] = None,
+         name: str = "custom") -> Workload:
+    """Build one workload.  ``lengths`` (list of (sq, sk)) makes a packed varlen batch;
+    ``key_offsets`` (seqlen_k values, fixed-length batches only) shapes the scores per key."""
     dv = head_dim if head_dim_v is None else head_dim_v
     scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
     cu = None
@@ -106,15 +114,24 @@ def make(batch: int, heads_q: int, heads_kv: int, seqlen_q: int, seqlen_k: int, 
         lens = [(seqlen_q, seqlen_k)] * batch
         total_q, total_k = batch * seqlen_q, batch * seqlen_k
     g = torch.Generator().manual_seed(seed)
+    mult = 1.0 if dtype == "bf16" else fp8_mult
+    xq = _randn(g, (total_q, heads_q, head_dim), mult * q_mult)
+    xk = _randn(g, (total_k, heads_kv, head_dim), mult)
+    xv = _randn(g, (total_k, heads_kv, dv), mult)
+    if key_offsets is not None:
+        offs = np.asarray(key_offsets, dtype=np.float64).reshape(-1)
+        if lengths is not None or offs.shape[0] != seqlen_k:
+            raise ValueError("key_offsets needs a fixed-length batch and one value per key")
+        b0 = torch.from_numpy(offs / (scale * math.log2(math.e))).float()
+        xq[:, :, 0] = 1.0
+        xk[:, :, 0] = b0.repeat(batch)[:, None]
     if dtype == "bf16":
-        q = _randn(g, (total_q, heads_q, head_dim), q_mult).to(torch.bfloat16)
-        k = _randn(g, (total_k, heads_kv, head_dim)).to(torch.bfloat16)
-        v = _randn(g, (total_k, heads_kv, dv)).to(torch.bfloat16)
+        q, k, v = (x.to(torch.bfloat16) for x in (xq, xk, xv))
         descales = None
     elif dtype == "e4m3":
-        q, dq = _quant_e4m3(_randn(g, (total_q, heads_q, head_dim), fp8_mult * q_mult))
-        k, dk = _quant_e4m3(_randn(g, (total_k, heads_kv, head_dim), fp8_mult))
-        v, dvs = _quant_e4m3(_randn(g, (total_k, heads_kv, dv), fp8_mult))
+        q, dq = _quant_e4m3(xq)
+        k, dk = _quant_e4m3(xk)
+        v, dvs = _quant_e4m3(xv)
         descales = np.array([dq, dk, dvs], dtype=np.float32)
     else:
         raise ValueError(dtype)

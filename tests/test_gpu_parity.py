@@ -221,6 +221,56 @@ def test_large_q_magnitude(schedule):
     full_check(w)
 
 
+def key_offset_pattern(pattern: str, sk: int) -> np.ndarray:
+    """Per-key score offsets in base-2 units.  Blocks of keys are visited from the last key
+    to the first, so 'jumpG' raises the running maximum of every row that sees keys on both
+    sides of sk/2 by G at once, 'rampA' by A every 64 keys, 'fall' lets it fall (scores of
+    later-visited keys underflow), 'saw' alternates high and low 64-key blocks."""
+    j = np.arange(sk, dtype=np.float64)
+    kind, amount = pattern.rstrip("0123456789."), pattern[len(pattern.rstrip("0123456789.")):]
+    a = float(amount) if amount else 0.0
+    if kind == "jump":
+        return np.where(j < sk // 2, a, 0.0)
+    if kind == "ramp":
+        return a * (sk - 1 - j) / 64.0
+    if kind == "fall":
+        return 6.0 * j / 64.0
+    if kind == "saw":
+        return np.where((j // 64) % 2 == 0, 12.0, 0.0)
+    raise ValueError(pattern)
+
+
+GROWTH_PATTERNS = ["jump3", "jump7.9", "jump8.1", "jump30", "ramp3", "ramp10", "fall", "saw"]
+
+
+@pytest.mark.parametrize("pattern", GROWTH_PATTERNS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 4, 2, 520, 520), (1, 8, 2, 4, 1000)], ids=["prefill", "decode"])
+def test_running_max_growth(shape, causal, pattern, schedule):
+    """Scores whose row maximum grows by less than, about and more than the lazy-rescale bound
+    (2^8) as key blocks are visited, in steps and ramps, or falls: the exponentials taken
+    against a stale maximum must be redone against the block maximum exactly when needed."""
+    b, hq, hkv, sq, sk = shape
+    w = fa_inputs.make(b, hq, hkv, sq, sk, 128, causal=causal, seed=80 + GROWTH_PATTERNS.index(pattern),
+                       key_offsets=key_offset_pattern(pattern, sk),
+                       name=f"growth_{pattern}_sq{sq}_sk{sk}_c{int(causal)}")
+    full_check(w)
+
+
+@pytest.mark.parametrize("pattern", GROWTH_PATTERNS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_running_max_growth(causal, pattern):
+    """As above for e4m3.  The fp8 matrix instruction's dot product keeps about 13 bits
+    relative to the score's magnitude (a causal row that sees one key has LSE = its scaled
+    score; at LSE = 55 its error is 6e-3), so the steep ramp runs over 256 keys, which keeps
+    |LSE| below about 30, where the fp8 LSE tolerance holds."""
+    s = 256 if pattern == "ramp10" else 520
+    w = fa_inputs.make(1, 4, 2, s, s, 128, causal=causal, seed=90 + GROWTH_PATTERNS.index(pattern),
+                       dtype="e4m3", key_offsets=key_offset_pattern(pattern, s),
+                       name=f"fp8_growth_{pattern}_s{s}_c{int(causal)}")
+    full_check(w)
+
+
 def test_gqa_equals_repeated_mha_on_gpu(schedule):
     w = fa_inputs.make(1, 8, 2, 257, 257, 128, causal=True, seed=62, name="gqa")
     o1, l1 = gpu_run(w)
