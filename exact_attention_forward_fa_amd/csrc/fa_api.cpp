@@ -111,9 +111,10 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   //  * schedule 2 (bf16): 4 waves with two query tiles each: 256 rows of one
   //    head, the full 512-register file (1 wave per SIMD); each LDS operand
   //    read feeds two MFMAs;
-  //  * schedule 3 (bf16, heads_q / heads_kv even): 8 waves in two groups of
-  //    four, 128 rows of two query heads that share a KV head, alternating
-  //    GEMM and softmax slots (ping-pong), 256 registers per lane;
+  //  * schedule 3 (bf16, heads_q / heads_kv even or 1): 8 waves in two groups
+  //    of four, 128 rows of two query heads that share a KV head -- or, for
+  //    heads_q == heads_kv, two adjacent 128-row tiles of one head --,
+  //    alternating GEMM and softmax slots (ping-pong), 256 registers per lane;
   //  * schedule 4 (bf16, heads_q / heads_kv * seqlen_q <= 32): decode -- all
   //    query rows of one KV head's group in the 32 columns of one tile, one
   //    workgroup per (sequence, KV head) whose 4 waves split the key range in
@@ -128,7 +129,7 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const int group = heads_q / heads_kv;
   const bool bf16 = dtype == FA_DTYPE_BF16;
   const bool wide_ok = bf16 && L.regs_per_simd_lane >= 512;
-  const bool pp_ok = bf16 && group % 2 == 0 && L.regs_per_simd_lane >= 512;
+  const bool pp_ok = bf16 && (group % 2 == 0 || group == 1) && L.regs_per_simd_lane >= 512;
   const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&
                          L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;
@@ -153,11 +154,14 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   }
   const int qt = sched == 2 ? 2 : 1;
   const int waves = sched == 3 ? 2 * fa::kWaves : fa::kWaves;
-  const int heads_per_wg = sched == 3 ? 2 : 1;
+  // schedule 3 with heads_q == heads_kv: two adjacent 128-row tiles of one
+  // head per workgroup instead of two heads
+  const bool mpair = sched == 3 && group == 1;
+  const int heads_per_wg = sched == 3 && !mpair ? 2 : 1;
   const int vgprs = 256 * qt;
   const int by_lds = (int)(L.lds_bytes_per_cu / lds);
   const int by_regs = (L.regs_per_simd_lane / vgprs) * L.simds_per_cu / waves;
-  out->tile_m = fa::kTileM * qt;
+  out->tile_m = fa::kTileM * (mpair ? 2 : qt);
   out->tile_n = fa::kTileN;
   out->waves = waves;
   out->kv_stages = fa::kStages;

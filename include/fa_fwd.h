@@ -201,9 +201,11 @@ typedef struct fa_plan {
  *   2  bf16: 4 waves with two query tiles each: 256 rows of one head, one wave
  *      per SIMD holding the full register file, every LDS operand read
  *      feeding two matrix instructions;
- *   3  bf16, heads_q / heads_kv even: 8 waves in two groups of four, 128 rows
- *      of two query heads that share a KV head (one K/V staging for both),
- *      the groups alternating matrix-core and softmax phases (ping-pong);
+ *   3  bf16, heads_q / heads_kv even or 1: 8 waves in two groups of four,
+ *      128 rows of two query heads that share a KV head, or (heads_q ==
+ *      heads_kv) two adjacent 128-row query tiles of one head (tile_m 256),
+ *      one K/V staging for both groups, the groups alternating matrix-core
+ *      and softmax phases (ping-pong);
  *   4  bf16, heads_q / heads_kv * seqlen_q <= 32 (decode): the (query head,
  *      row) pairs of one KV head in the 32 columns of one tile, one workgroup
  *      per (sequence, KV head) whose 4 waves split the key range and merge

@@ -199,11 +199,16 @@ def test_plan_gfx950():
     # 16 (batch, kv-head) pairs = 2 rounds over 8 XCDs, x 64 tiles x 2 head pairs per kv-head
     assert p.m_tiles == 64 and p.num_workgroups == 2 * 8 * 64 * 2
     p64 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 2, 2, 256, 256, False, 64, 64, False)
-    # heads_q / heads_kv = 1: one query tile per wave; 2 (batch, kv-head) pairs dealt to 8
-    # XCDs: one padded round of 8 pairs x 2 tiles x 1 head
+    # heads_q / heads_kv = 1: still the ping-pong schedule, its two groups on two adjacent
+    # 128-row tiles of one head (256 rows per workgroup); 2 (batch, kv-head) pairs dealt to 8
+    # XCDs: one padded round of 8 pairs x 1 tile pair x 1 head
     assert (p64.schedule, p64.tile_m, p64.query_tiles, p64.wg_per_cu, p64.vgprs_per_lane) == \
-        (1, 128, 1, 2, 256)
-    assert p64.m_tiles == 2 and p64.num_workgroups == 8 * 2 and p64.lds_bytes < p.lds_bytes
+        (3, 256, 1, 1, 256)
+    assert (p64.waves, p64.heads_per_workgroup) == (8, 1)
+    assert p64.m_tiles == 1 and p64.num_workgroups == 8 * 1 and p64.lds_bytes < p.lds_bytes
+    # 300 rows: 3 tiles of 128 rows = 2 tile pairs (the upper tile of the last pair is empty)
+    p300 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 4, 4, 300, 300, True, 128, 128, False)
+    assert (p300.schedule, p300.m_tiles, p300.num_workgroups) == (3, 2, 8 * 2)
     # fp8 always uses schedule 1
     p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 32, 8, 16384, 16384, False, 128, 128, True)
     assert (p8.schedule, p8.tile_m, p8.query_tiles, p8.lds_bytes) == (1, 128, 1, 32 * KIB)

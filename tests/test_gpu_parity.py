@@ -14,8 +14,8 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(params=[1, 2, 3, 4], ids=["sched1", "sched2", "sched3", "sched4"])
 def schedule(request):
     """Force each bf16 schedule (1: one query tile per wave; 2: two; 3: 8-wave ping-pong,
-    where heads_q / heads_kv is even; 4: decode, where heads_q / heads_kv * seqlen_q <= 32;
-    else 1) for the test."""
+    where heads_q / heads_kv is even (two heads per workgroup) or 1 (two adjacent query tiles
+    of one head); 4: decode, where heads_q / heads_kv * seqlen_q <= 32; else 1) for the test."""
     import exact_attention_forward_fa_amd as fa
 
     fa.fa_set_schedule(request.param)
@@ -113,7 +113,8 @@ def test_varlen_equals_per_sequence_calls(schedule):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 4, 4, 300, 300), (1, 8, 2, 200, 517), (1, 4, 1, 517, 200),
-                                   (3, 2, 2, 1, 1), (1, 2, 2, 1, 333), (1, 32, 1, 130, 130)])
+                                   (3, 2, 2, 1, 1), (1, 2, 2, 1, 333), (1, 32, 1, 130, 130),
+                                   (1, 2, 2, 600, 250), (2, 3, 3, 250, 640)])
 def test_ragged_shapes(shape, causal, d, schedule):
     b, hq, hkv, sq, sk = shape
     w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq * 7 + sk + d,
