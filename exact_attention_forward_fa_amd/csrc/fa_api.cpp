@@ -111,7 +111,7 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   //  * schedule 2 (bf16): 4 waves with two query tiles each: 256 rows of one
   //    head, the full 512-register file (1 wave per SIMD); each LDS operand
   //    read feeds two MFMAs;
-  //  * schedule 3 (bf16, heads_q / heads_kv even or 1): 8 waves in two groups
+  //  * schedule 3 (bf16, heads_q / heads_kv even, or 1 without varlen): 8 waves in two groups
   //    of four, 128 rows of two query heads that share a KV head -- or, for
   //    heads_q == heads_kv, two adjacent 128-row tiles of one head --,
   //    alternating GEMM and softmax slots (ping-pong), 256 registers per lane;
@@ -129,7 +129,12 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const int group = heads_q / heads_kv;
   const bool bf16 = dtype == FA_DTYPE_BF16;
   const bool wide_ok = bf16 && L.regs_per_simd_lane >= 512;
-  const bool pp_ok = bf16 && (group % 2 == 0 || group == 1) && L.regs_per_simd_lane >= 512;
+  // MHA takes the ping-pong as tile pairs only for fixed lengths: on packed
+  // varlen batches the 256-row granularity (half-empty last pairs, the lower
+  // tile's masked blocks on every diagonal) measured 5 % slower than
+  // schedule 1's two 128-row workgroups per CU
+  const bool pp_ok = bf16 && (group % 2 == 0 || (group == 1 && !varlen)) &&
+                     L.regs_per_simd_lane >= 512;
   const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&
                          L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;

@@ -201,7 +201,8 @@ typedef struct fa_plan {
  *   2  bf16: 4 waves with two query tiles each: 256 rows of one head, one wave
  *      per SIMD holding the full register file, every LDS operand read
  *      feeding two matrix instructions;
- *   3  bf16, heads_q / heads_kv even or 1: 8 waves in two groups of four,
+ *   3  bf16, heads_q / heads_kv even, or 1 for fixed lengths (varlen == 0):
+ *      8 waves in two groups of four,
  *      128 rows of two query heads that share a KV head, or (heads_q ==
  *      heads_kv) two adjacent 128-row query tiles of one head (tile_m 256),
  *      one K/V staging for both groups, the groups alternating matrix-core

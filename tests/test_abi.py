@@ -207,8 +207,11 @@ def test_plan_gfx950():
     assert (p64.waves, p64.heads_per_workgroup) == (8, 1)
     assert p64.m_tiles == 1 and p64.num_workgroups == 8 * 1 and p64.lds_bytes < p.lds_bytes
     # 300 rows: 3 tiles of 128 rows = 2 tile pairs (the upper tile of the last pair is empty)
-    p300 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 4, 4, 300, 300, True, 128, 128, False)
+    p300 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 4, 4, 300, 300, False, 128, 128, True)
     assert (p300.schedule, p300.m_tiles, p300.num_workgroups) == (3, 2, 8 * 2)
+    # packed varlen MHA stays on schedule 1 (128-row tiles, two workgroups per CU)
+    pv = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 18, 16, 16, 4096, 4608, True, 128, 128, True)
+    assert (pv.schedule, pv.tile_m, pv.wg_per_cu) == (1, 128, 2)
     # fp8 always uses schedule 1
     p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 32, 8, 16384, 16384, False, 128, 128, True)
     assert (p8.schedule, p8.tile_m, p8.query_tiles, p8.lds_bytes) == (1, 128, 1, 32 * KIB)
