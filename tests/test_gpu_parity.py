@@ -440,3 +440,57 @@ def test_kvcache_fp8():
     case = fa_inputs.make_kvcache(2, 130, 70, 1024, [0, 400], 4, 2, 128, causal=True, seed=86,
                                   dtype="e4m3")
     kvcache_check(case, "kv_fp8")
+
+
+# ------------------------------------------------------------ graph capture
+
+@pytest.mark.parametrize("case", ["gqa_pingpong", "mha_pairs", "varlen", "fp8", "decode"])
+def test_graph_capture_replays(case):
+    """fa_fwd allocates nothing and launches only kernels on the caller's stream, so it can be
+    captured into a HIP graph: every replay (with other work on the device between replays)
+    gives the eager call's O and LSE bit for bit."""
+    import exact_attention_forward_fa_amd as fa
+
+    if case == "gqa_pingpong":
+        w = fa_inputs.make(2, 8, 2, 300, 517, 128, causal=True, seed=71, name="graph_gqa")
+    elif case == "mha_pairs":
+        w = fa_inputs.make(2, 3, 3, 600, 600, 64, causal=True, seed=72, name="graph_mha")
+    elif case == "varlen":
+        w = fa_inputs.make(0, 4, 2, 0, 0, 128, causal=True, seed=73,
+                           lengths=[(300, 517), (1, 64), (129, 100), (255, 256)], name="graph_varlen")
+    elif case == "fp8":
+        w = fa_inputs.make(1, 4, 4, 260, 260, 128, causal=True, seed=74, dtype="e4m3", name="graph_fp8")
+    else:
+        w = fa_inputs.make(4, 16, 4, 1, 1000, 128, causal=True, seed=75, name="graph_decode")
+    q, k, v, cu, ds = to_device(w)
+    total_q = q.shape[0]
+    hq, dv = w.heads_q, w.head_dim_v
+
+    def call(o, lse):
+        fa.fa_fwd(q, k, v, o, lse, w.batch, hq, w.heads_kv, w.seqlen_q, w.seqlen_k, cu,
+                  w.head_dim, dv, w.softmax_scale, int(w.causal), ds)
+
+    say(f"[gpu] graph capture {w.name}")
+    o_ref = torch.empty(total_q, hq, dv, dtype=torch.bfloat16, device="cuda")
+    lse_ref = torch.empty(hq, total_q, dtype=torch.float32, device="cuda")
+    call(o_ref, lse_ref)
+    o = torch.empty_like(o_ref)
+    lse = torch.empty_like(lse_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(o, lse)  # warm-up on the capture stream, as torch's capture expects
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(o, lse)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()  # other work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), f"replay {rep}: O differs"
+        assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32)), f"replay {rep}: LSE differs"
