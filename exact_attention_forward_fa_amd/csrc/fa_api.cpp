@@ -120,7 +120,8 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   //    workgroup per (sequence, KV head) whose 4 waves split the key range in
   //    32-key blocks, each with a 2-slot K and V ring in LDS, one wave per
   //    SIMD.
-  // Automatic: 4 where it applies, else 3 where it applies, else 1.
+  // Automatic: 4 where it applies, else 3 where it applies with at least one
+  // workgroup per CU, else 1.
   // fa_set_schedule forces one (falling back to 1 where it does not apply).
   const int64_t lds = fa::lds_bytes(head_dim, dtype == FA_DTYPE_E4M3 ? 1 : 2);
   if (lds > L.lds_bytes_per_block) return FA_ERR_UNSUPPORTED;
@@ -135,11 +136,20 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   // schedule 1's two 128-row workgroups per CU
   const bool pp_ok = bf16 && (group % 2 == 0 || (group == 1 && !varlen)) &&
                      L.regs_per_simd_lane >= 512;
+  // The ping-pong kernel puts twice the rows of schedule 1 into a workgroup
+  // (and one workgroup on a CU): where that leaves CUs idle, schedule 1's
+  // finer grid finishes first (the 2-head x 256-row case measured 8.6 us
+  // against 6.2 us), so the automatic choice takes it only for grids of at
+  // least one workgroup per CU.
+  const int64_t pp_rows = group == 1 ? 2LL * fa::kTileM : fa::kTileM;
+  const int64_t pp_items = (int64_t)batch * heads_kv * (group == 1 ? 1 : group / 2) *
+                           ((seqlen_q + pp_rows - 1) / pp_rows);
+  const bool pp_auto = pp_ok && pp_items >= L.num_cus;
   const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&
                          L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;
   const int forced = g_schedule.load(std::memory_order_relaxed);
-  int sched = forced ? forced : (decode_ok ? 4 : pp_ok ? 3 : 1);
+  int sched = forced ? forced : (decode_ok ? 4 : pp_auto ? 3 : 1);
   if ((sched == 2 && !wide_ok) || (sched == 3 && !pp_ok) || (sched == 4 && !decode_ok)) sched = 1;
   if (sched == 4) {
     out->tile_m = 32;  // (query head, row) columns of one tile

@@ -12,7 +12,10 @@ constexpr int kTileN = 64;   // keys per main-loop step
 constexpr int kWaves = 4;    // wavefronts per workgroup
 constexpr int kStages = 2;   // K/V LDS buffers
 constexpr int kXcds = 8;     // XCDs of an MI355X; workgroups go round-robin over them
-constexpr int kDecodeSlots = 2;  // K and V LDS ring slots per wave of the decode kernel
+#ifndef DEC_SLOTS
+#define DEC_SLOTS 2
+#endif
+constexpr int kDecodeSlots = DEC_SLOTS;  // K and V LDS ring slots per wave of the decode kernel
 
 // LDS per workgroup: K and V blocks of kTileN rows of d*2 bytes (no padding;
 // bank conflicts are avoided by swizzling 16-byte columns), double-buffered.

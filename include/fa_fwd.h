@@ -211,8 +211,9 @@ typedef struct fa_plan {
  *      row) pairs of one KV head in the 32 columns of one tile, one workgroup
  *      per (sequence, KV head) whose 4 waves split the key range and merge
  *      their partial softmax states at the end.
- * The plan uses 4 where it applies, else 3 where it applies, else 1, unless
- * fa_set_schedule forces one.
+ * The plan uses 4 where it applies, else 3 where it applies and its grid has
+ * at least one workgroup per CU (`dev->num_cus`; smaller grids finish first
+ * on schedule 1's finer tiles), else 1, unless fa_set_schedule forces one.
  */
 int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
                 int varlen, int head_dim, int head_dim_v, int causal,

@@ -198,17 +198,23 @@ def test_plan_gfx950():
     assert p.lds_bytes == 64 * KIB
     # 16 (batch, kv-head) pairs = 2 rounds over 8 XCDs, x 64 tiles x 2 head pairs per kv-head
     assert p.m_tiles == 64 and p.num_workgroups == 2 * 8 * 64 * 2
-    p64 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 2, 2, 256, 256, False, 64, 64, False)
-    # heads_q / heads_kv = 1: still the ping-pong schedule, its two groups on two adjacent
-    # 128-row tiles of one head (256 rows per workgroup); 2 (batch, kv-head) pairs dealt to 8
-    # XCDs: one padded round of 8 pairs x 1 tile pair x 1 head
-    assert (p64.schedule, p64.tile_m, p64.query_tiles, p64.wg_per_cu, p64.vgprs_per_lane) == \
+    # MHA (heads_q / heads_kv = 1) with at least one workgroup per CU: still the ping-pong
+    # schedule, its two groups on two adjacent 128-row tiles of one head (256 rows per
+    # workgroup); 64 (batch, head) pairs = 8 rounds over the XCDs x 4 tile pairs
+    pm = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 1024, 1024, False, 128, 128, True)
+    assert (pm.schedule, pm.tile_m, pm.query_tiles, pm.wg_per_cu, pm.vgprs_per_lane) == \
         (3, 256, 1, 1, 256)
-    assert (p64.waves, p64.heads_per_workgroup) == (8, 1)
-    assert p64.m_tiles == 1 and p64.num_workgroups == 8 * 1 and p64.lds_bytes < p.lds_bytes
-    # 300 rows: 3 tiles of 128 rows = 2 tile pairs (the upper tile of the last pair is empty)
-    p300 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 4, 4, 300, 300, False, 128, 128, True)
-    assert (p300.schedule, p300.m_tiles, p300.num_workgroups) == (3, 2, 8 * 2)
+    assert (pm.waves, pm.heads_per_workgroup, pm.m_tiles, pm.num_workgroups) == (8, 1, 4, 8 * 8 * 4)
+    # 1100 rows: 9 tiles of 128 rows = 5 tile pairs (the upper tile of the last pair is empty)
+    p1100 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 1100, 1100, False, 128, 128, True)
+    assert (p1100.schedule, p1100.m_tiles, p1100.num_workgroups) == (3, 5, 8 * 8 * 5)
+    # fewer ping-pong workgroups than CUs: schedule 1's finer grid (one query tile per wave);
+    # 2 (batch, kv-head) pairs dealt to 8 XCDs: one padded round of 8 pairs x 2 tiles x 1 head
+    p64 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 2, 2, 256, 256, False, 64, 64, False)
+    assert (p64.schedule, p64.tile_m, p64.query_tiles, p64.wg_per_cu, p64.vgprs_per_lane) == \
+        (1, 128, 1, 2, 256)
+    assert p64.m_tiles == 2 and p64.num_workgroups == 8 * 2 and p64.lds_bytes < p.lds_bytes
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 2, 512, 512, False, 128, 128, True).schedule == 1
     # packed varlen MHA stays on schedule 1 (128-row tiles, two workgroups per CU)
     pv = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 18, 16, 16, 4096, 4608, True, 128, 128, True)
     assert (pv.schedule, pv.tile_m, pv.wg_per_cu) == (1, 128, 2)
@@ -224,7 +230,8 @@ def test_plan_gfx950():
     assert pd.lds_bytes == 4 * (2 * 2 * 32 * 128 * 2)
     # 8 heads x 4 rows = 32 columns still fits; 8 x 5 does not
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 4, 100, False, 64, 64, False).schedule == 4
-    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 5, 100, False, 64, 64, False).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 5, 100, False, 64, 64, False).schedule == 1
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 64, 8, 1, 5, 100, False, 64, 64, False).schedule == 3
     # fp8 never takes it
     assert fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 32, 32, 8, 1, 8192, False, 128, 128, True).schedule == 1
 

@@ -160,14 +160,16 @@ def test_exp2_offload(shape, every):
     import exact_attention_forward_fa_amd as fa
 
     b, hq, hkv, sq, sk, d, causal = shape
-    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, b, hq, hkv, sq, sk, False, d, d, causal).schedule == 3
     w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq + sk + every,
                        name=f"exp2_offload{every}_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}")
+    fa.fa_set_schedule(3)  # small grids default to schedule 1
     fa.fa_set_exp2_offload(every)
     try:
+        assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, b, hq, hkv, sq, sk, False, d, d, causal).schedule == 3
         full_check(w)
     finally:
         fa.fa_set_exp2_offload(0)
+        fa.fa_set_schedule(0)
 
 
 def test_exp2_offload_large_q():
@@ -176,11 +178,13 @@ def test_exp2_offload_large_q():
 
     w = fa_inputs.make(1, 4, 2, 256, 256, 128, causal=True, seed=65, q_mult=50.0,
                        name="exp2_offload_q_x50")
+    fa.fa_set_schedule(3)
     fa.fa_set_exp2_offload(4)
     try:
         full_check(w)
     finally:
         fa.fa_set_exp2_offload(0)
+        fa.fa_set_schedule(0)
 
 
 @pytest.mark.parametrize("shape", [(8, 8, 2, 1, 4096), (4, 16, 4, 3, 2500)])
