@@ -111,9 +111,10 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   //  * schedule 2 (bf16): 4 waves with two query tiles each: 256 rows of one
   //    head, the full 512-register file (1 wave per SIMD); each LDS operand
   //    read feeds two MFMAs;
-  //  * schedule 3 (bf16, heads_q / heads_kv even, or 1 without varlen): 8 waves in two groups
-  //    of four, 128 rows of two query heads that share a KV head -- or, for
-  //    heads_q == heads_kv, two adjacent 128-row tiles of one head --,
+  //  * schedule 3 (bf16, heads_q / heads_kv even, or odd without varlen): 8
+  //    waves in two groups of four, 128 rows of two query heads that share a
+  //    KV head -- or, for an odd heads_q / heads_kv (1: MHA), two adjacent
+  //    128-row tiles of one head --,
   //    alternating GEMM and softmax slots (ping-pong), 256 registers per lane;
   //  * schedule 4 (bf16, heads_q / heads_kv * seqlen_q <= 32): decode -- all
   //    query rows of one KV head's group in the 32 columns of one tile, one
@@ -130,21 +131,26 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const int group = heads_q / heads_kv;
   const bool bf16 = dtype == FA_DTYPE_BF16;
   const bool wide_ok = bf16 && L.regs_per_simd_lane >= 512;
-  // MHA takes the ping-pong as tile pairs only for fixed lengths: on packed
+  // Odd groups (MHA) take the ping-pong as tile pairs only for fixed lengths: on packed
   // varlen batches the 256-row granularity (half-empty last pairs, the lower
   // tile's masked blocks on every diagonal) measured 5 % slower than
   // schedule 1's two 128-row workgroups per CU
-  const bool pp_ok = bf16 && (group % 2 == 0 || (group == 1 && !varlen)) &&
+  const bool pp_ok = bf16 && (group % 2 == 0 || !varlen) &&
                      L.regs_per_simd_lane >= 512;
   // The ping-pong kernel puts twice the rows of schedule 1 into a workgroup
   // (and one workgroup on a CU): where that leaves CUs idle, schedule 1's
   // finer grid finishes first (the 2-head x 256-row case measured 8.6 us
   // against 6.2 us), so the automatic choice takes it only for grids of at
   // least one workgroup per CU.
-  const int64_t pp_rows = group == 1 ? 2LL * fa::kTileM : fa::kTileM;
-  const int64_t pp_items = (int64_t)batch * heads_kv * (group == 1 ? 1 : group / 2) *
+  const int64_t pp_rows = group % 2 ? 2LL * fa::kTileM : fa::kTileM;
+  const int64_t pp_items = (int64_t)batch * heads_kv * (group % 2 ? group : group / 2) *
                            ((seqlen_q + pp_rows - 1) / pp_rows);
-  const bool pp_auto = pp_ok && pp_items >= L.num_cus;
+  // Causal tile pairs give the lower tile two fully masked key blocks per
+  // pair; measured against schedule 1 they win at 8192 rows (+3 %) and on a
+  // single round of pairs (MHA 4 x 16 x 1024: +10 %), lose at 1024-4096 rows
+  // over several rounds (-6 to -14 %); non-causal pairs win (+5 to +9 %).
+  const bool pairs_ok = group % 2 == 0 || !causal || seqlen_q >= 8192 || pp_items <= L.num_cus;
+  const bool pp_auto = pp_ok && pp_items >= L.num_cus && pairs_ok;
   const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&
                          L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;
@@ -169,9 +175,9 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   }
   const int qt = sched == 2 ? 2 : 1;
   const int waves = sched == 3 ? 2 * fa::kWaves : fa::kWaves;
-  // schedule 3 with heads_q == heads_kv: two adjacent 128-row tiles of one
-  // head per workgroup instead of two heads
-  const bool mpair = sched == 3 && group == 1;
+  // schedule 3 with an odd heads_q / heads_kv: two adjacent 128-row tiles of
+  // one head per workgroup instead of two heads
+  const bool mpair = sched == 3 && group % 2 == 1;
   const int heads_per_wg = sched == 3 && !mpair ? 2 : 1;
   const int vgprs = 256 * qt;
   const int by_lds = (int)(L.lds_bytes_per_cu / lds);

@@ -5,7 +5,7 @@
 //     rows of one (sequence, head), two workgroups per CU;
 //  2. fa_fwd_bf16_kernel<.., QG = 2>: 256 rows, one wave per SIMD;
 //  3. fa_fwd_bf16_pp_kernel: 8 waves, two query heads of one KV head (or,
-//     with one query head per KV head, two adjacent query tiles of it), the
+//     with an odd number of query heads per KV head, two adjacent query tiles of one), the
 //     two groups of waves alternating GEMM and softmax phases (ping-pong);
 //  4. fa_fwd_bf16_decode_kernel: a KV head's (query head, row) pairs in one
 //     32-column tile, the 4 waves splitting the key range.
@@ -612,11 +612,11 @@ void fa_fwd_bf16_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong schedule (bf16; heads_q / heads_kv even, or 1).  A workgroup of 8
-// waves (two per SIMD) takes one 128-row query tile of TWO query heads that
-// share a KV head -- or, with one query head per KV head, two adjacent
-// 128-row tiles of one head -- so both halves walk the same key blocks out of
-// one K/V staging.
+// Ping-pong schedule (bf16).  A workgroup of 8 waves (two per SIMD) takes one
+// 128-row query tile of TWO query heads that share a KV head -- or, with an
+// odd number of query heads per KV head (1 for MHA), two adjacent 128-row
+// tiles of one head -- so both halves walk the same key blocks out of one K/V
+// staging.
 // Waves 0-3 (group A, first head) and 4-7 (group B, second head) alternate
 // between a GEMM slot -- the QK^T of the next block and the P V of the current
 // one, with all their LDS operand reads -- and a softmax slot (VALU and the
@@ -661,13 +661,13 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   const int hf = lane >> 5;
 
   // ---- work item: the XCD deal of the 4-wave kernel, with pairs of query
-  // heads in place of query heads.  Without a second query head per KV head
-  // (heads_q == heads_kv) the two groups take two adjacent 128-row query
-  // tiles of one head instead (p.m_tiles then counts tile pairs): they still
-  // read the same K/V blocks, those of the upper tile, whose extra causal
-  // blocks are fully masked for the lower one.
-  const bool mpair = p.group == 1;
-  const int hpairs = mpair ? 1 : p.group >> 1;
+  // heads in place of query heads.  With an odd number of query heads per
+  // KV head (1 for MHA) the two groups take two adjacent 128-row query tiles
+  // of one head instead (p.m_tiles then counts tile pairs): they still read
+  // the same K/V blocks, those of the upper tile, whose extra causal blocks
+  // are fully masked for the lower one.
+  const bool mpair = p.group & 1;
+  const int hpairs = mpair ? p.group : p.group >> 1;  // slots per (tile, KV head)
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per_pair = p.m_tiles * hpairs;
@@ -678,7 +678,8 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   const int b = pair / p.hkv;
   const int mrev = within / hpairs;
   const int g = pair - b * p.hkv;
-  const int head = mpair ? g : g * p.group + 2 * (within - mrev * hpairs) + grp;
+  const int head = mpair ? g * p.group + (within - mrev * hpairs)
+                         : g * p.group + 2 * (within - mrev * hpairs) + grp;
   const int mblk = CAUSAL ? (p.m_tiles - 1 - mrev) : mrev;
   const SeqInfo si = seq_info(p, b);
   const int m0_wg = mpair ? 2 * mblk * TM : mblk * TM;  // the workgroup's first row

@@ -201,10 +201,10 @@ typedef struct fa_plan {
  *   2  bf16: 4 waves with two query tiles each: 256 rows of one head, one wave
  *      per SIMD holding the full register file, every LDS operand read
  *      feeding two matrix instructions;
- *   3  bf16, heads_q / heads_kv even, or 1 for fixed lengths (varlen == 0):
- *      8 waves in two groups of four,
- *      128 rows of two query heads that share a KV head, or (heads_q ==
- *      heads_kv) two adjacent 128-row query tiles of one head (tile_m 256),
+ *   3  bf16, heads_q / heads_kv even, or odd for fixed lengths (varlen ==
+ *      0): 8 waves in two groups of four, 128 rows of two query heads that
+ *      share a KV head, or (odd heads_q / heads_kv, e.g. 1) two adjacent
+ *      128-row query tiles of one head (tile_m 256),
  *      one K/V staging for both groups, the groups alternating matrix-core
  *      and softmax phases (ping-pong);
  *   4  bf16, heads_q / heads_kv * seqlen_q <= 32 (decode): the (query head,
@@ -213,7 +213,9 @@ typedef struct fa_plan {
  *      their partial softmax states at the end.
  * The plan uses 4 where it applies, else 3 where it applies and its grid has
  * at least one workgroup per CU (`dev->num_cus`; smaller grids finish first
- * on schedule 1's finer tiles), else 1, unless fa_set_schedule forces one.
+ * on schedule 1's finer tiles) -- with tile pairs under causal masking only
+ * from 8192 query rows or for a single round of pairs --, else 1, unless
+ * fa_set_schedule forces one.
  */
 int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
                 int varlen, int head_dim, int head_dim_v, int causal,

@@ -206,7 +206,7 @@ def test_plan_gfx950():
         (3, 256, 1, 1, 256)
     assert (pm.waves, pm.heads_per_workgroup, pm.m_tiles, pm.num_workgroups) == (8, 1, 4, 8 * 8 * 4)
     # 1100 rows: 9 tiles of 128 rows = 5 tile pairs (the upper tile of the last pair is empty)
-    p1100 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 1100, 1100, False, 128, 128, True)
+    p1100 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 1100, 1100, False, 128, 128, False)
     assert (p1100.schedule, p1100.m_tiles, p1100.num_workgroups) == (3, 5, 8 * 8 * 5)
     # fewer ping-pong workgroups than CUs: schedule 1's finer grid (one query tile per wave);
     # 2 (batch, kv-head) pairs dealt to 8 XCDs: one padded round of 8 pairs x 2 tiles x 1 head
@@ -215,6 +215,11 @@ def test_plan_gfx950():
         (1, 128, 1, 2, 256)
     assert p64.m_tiles == 2 and p64.num_workgroups == 8 * 2 and p64.lds_bytes < p.lds_bytes
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 2, 512, 512, False, 128, 128, True).schedule == 1
+    # causal tile pairs over several rounds below 8192 rows: schedule 1; non-causal: pairs
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 2048, 2048, False, 128, 128, True).schedule == 1
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 2048, 2048, False, 128, 128, False).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 24, 8, 8192, 8192, False, 128, 128, True).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 24, 8, 2048, 2048, False, 128, 128, True).schedule == 1
     # packed varlen MHA stays on schedule 1 (128-row tiles, two workgroups per CU)
     pv = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 18, 16, 16, 4096, 4608, True, 128, 128, True)
     assert (pv.schedule, pv.tile_m, pv.wg_per_cu) == (1, 128, 2)
@@ -248,10 +253,15 @@ def test_schedule_override():
         assert (p.schedule, p.tile_m, p.query_tiles, p.m_tiles, p.wg_per_cu, p.vgprs_per_lane) == \
             (2, 256, 2, 32, 1, 512)
         assert p.num_workgroups == 2 * 8 * 32 * 4
-        # schedule 3 needs an even heads_q / heads_kv: falls back to 1
+        # schedule 3 with an odd heads_q / heads_kv: two adjacent query tiles of one head
         fa.fa_set_schedule(3)
         odd = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 3, 1, 300, 300, False, 64, 64, False)
-        assert (odd.schedule, odd.waves, odd.heads_per_workgroup) == (1, 4, 1)
+        assert (odd.schedule, odd.waves, odd.heads_per_workgroup, odd.tile_m) == (3, 8, 1, 256)
+        # 2 tile pairs x 3 heads per kv-head, one padded round of 8 (batch, kv-head) pairs
+        assert (odd.m_tiles, odd.num_workgroups) == (2, 8 * 2 * 3)
+        # ... but not for packed varlen batches: falls back to 1
+        oddv = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 3, 1, 300, 300, True, 64, 64, False)
+        assert (oddv.schedule, oddv.waves, oddv.heads_per_workgroup) == (1, 4, 1)
         # fp8 always uses 1
         p8 = fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 1, 2, 1, 300, 300, False, 64, 64, False)
         assert p8.schedule == 1

@@ -114,7 +114,7 @@ def test_varlen_equals_per_sequence_calls(schedule):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 4, 4, 300, 300), (1, 8, 2, 200, 517), (1, 4, 1, 517, 200),
                                    (3, 2, 2, 1, 1), (1, 2, 2, 1, 333), (1, 32, 1, 130, 130),
-                                   (1, 2, 2, 600, 250), (2, 3, 3, 250, 640)])
+                                   (1, 2, 2, 600, 250), (2, 3, 3, 250, 640), (1, 6, 2, 300, 520)])
 def test_ragged_shapes(shape, causal, d, schedule):
     b, hq, hkv, sq, sk = shape
     w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq * 7 + sk + d,
