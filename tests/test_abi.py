@@ -205,9 +205,9 @@ def test_plan_gfx950():
     assert (pm.schedule, pm.tile_m, pm.query_tiles, pm.wg_per_cu, pm.vgprs_per_lane) == \
         (3, 256, 1, 1, 256)
     assert (pm.waves, pm.heads_per_workgroup, pm.m_tiles, pm.num_workgroups) == (8, 1, 4, 8 * 8 * 4)
-    # 1100 rows: 9 tiles of 128 rows = 5 tile pairs (the upper tile of the last pair is empty)
-    p1100 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 1100, 1100, False, 128, 128, False)
-    assert (p1100.schedule, p1100.m_tiles, p1100.num_workgroups) == (3, 5, 8 * 8 * 5)
+    # 2100 rows: 17 tiles of 128 rows = 9 tile pairs (the upper tile of the last pair is empty)
+    p2100 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 2100, 2100, False, 128, 128, False)
+    assert (p2100.schedule, p2100.m_tiles, p2100.num_workgroups) == (3, 9, 8 * 8 * 9)
     # fewer ping-pong workgroups than CUs: schedule 1's finer grid (one query tile per wave);
     # 2 (batch, kv-head) pairs dealt to 8 XCDs: one padded round of 8 pairs x 2 tiles x 1 head
     p64 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 2, 2, 256, 256, False, 64, 64, False)
@@ -220,6 +220,10 @@ def test_plan_gfx950():
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 2048, 2048, False, 128, 128, False).schedule == 3
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 24, 8, 8192, 8192, False, 128, 128, True).schedule == 3
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 24, 8, 2048, 2048, False, 128, 128, True).schedule == 1
+    # head pairs below 2048 rows over several rounds: schedule 1; one round or 2048+: ping-pong
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 8, 32, 8, 1024, 1024, False, 128, 128, True).schedule == 1
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 32, 8, 2048, 2048, False, 128, 128, True).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 32, 8, 1024, 1024, False, 128, 128, True).schedule == 3
     # packed varlen MHA stays on schedule 1 (128-row tiles, two workgroups per CU)
     pv = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 18, 16, 16, 4096, 4608, True, 128, 128, True)
     assert (pv.schedule, pv.tile_m, pv.wg_per_cu) == (1, 128, 2)
