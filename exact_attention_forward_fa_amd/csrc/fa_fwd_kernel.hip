@@ -655,7 +655,11 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int grp = wave >> 2;  // 0: group A, 1: group B
-  const int wv = wave & 3;    // 32-row slice of the tile
+  // 32-row slice of the tile; group B takes the slices in reverse order, so
+  // that each SIMD holds a low and a high slice (waves w and w + 4 share one)
+  // and the causal diagonal's fully masked blocks, which the low slices skip,
+  // lighten every SIMD alike
+  const int wv = grp == 0 ? (wave & 3) : 3 - (wave & 3);
   const int lane = tid & 63;
   const int r32 = lane & 31;
   const int hf = lane >> 5;
@@ -773,6 +777,17 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // Causal: the top ktop blocks hold no admissible key for any row of this
+  // wave (its last row sees keys up to m0 + 32 wv + 31 + diag); they are
+  // skipped -- scores, softmax and P V -- in the first steps, which run with
+  // these per-wave checks (ks of them, bounded by the workgroup's lowest row).
+  int ktop = 0, ks = 0;
+  if (CAUSAL) {
+    const int last = m0 + wv * 32 + 31 + diag;
+    ktop = last < 0 ? N : max(0, N - 1 - last / TN);
+    const int wg_last = m0_wg + 31 + diag;
+    ks = wg_last < 0 ? N + 1 : min(N + 1, max(0, N - 1 - wg_last / TN) + 1);
+  }
   const int thr = CAUSAL ? min(si.sk, m0 + diag + 1) : si.sk;
   const int n_plain = thr <= 0 ? 0 : min(N, thr / TN);  // blocks below n_plain need no mask
 
@@ -869,8 +884,8 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   // The four LDS regions are distinct within a step; __restrict__ says so,
   // which keeps the compiler from waiting for the loads before LDS reads.
   auto step = [&](const int k, const char* __restrict__ kread, const char* __restrict__ vread,
-                  char* __restrict__ kdst, char* __restrict__ vdst, auto qk_tag, auto pv_tag)
-      __attribute__((always_inline)) {
+                  char* __restrict__ kdst, char* __restrict__ vdst, auto qk_tag, auto pv_tag,
+                  auto skip_tag) __attribute__((always_inline)) {
     // Each wave's own direct-to-LDS loads must be complete before the barrier
     // for the other waves to read them.  The wait is written out: the
     // barrier's fence does not oblige the compiler to wait for loads, and in
@@ -889,15 +904,33 @@ void fa_fwd_bf16_pp_kernel(Params p) {
     // matrix instructions and their LDS reads need.  The s_setprio
     // instructions also keep the compiler from mixing the two phases' code.
     // Measured 1.6 % faster than a barrier between the phases.
+    // with skips (first steps, causal): block N-1-k has no admissible key for
+    // this wave when k < ktop, block N-k when k <= ktop
+    const bool chk = decltype(skip_tag)::value;
+    const bool sk_q = chk && k < ktop, sk_p = chk && k <= ktop;
+    auto gemm_sk = [&]() __attribute__((always_inline)) {
+      constexpr bool Q = decltype(qk_tag)::value, PV = decltype(pv_tag)::value;
+      if (!chk) {
+        gemm(kread, vread, qk_tag, pv_tag);
+      } else if (Q && PV) {
+        if (!sk_q && !sk_p) gemm(kread, vread, BoolTag<true>{}, BoolTag<true>{});
+        else if (!sk_q) gemm(kread, vread, BoolTag<true>{}, BoolTag<false>{});
+        else if (!sk_p) gemm(kread, vread, BoolTag<false>{}, BoolTag<true>{});
+      } else if (Q) {
+        if (!sk_q) gemm(kread, vread, BoolTag<true>{}, BoolTag<false>{});
+      } else if (PV) {
+        if (!sk_p) gemm(kread, vread, BoolTag<false>{}, BoolTag<true>{});
+      }
+    };
     if (grp == 0) {
       __builtin_amdgcn_s_setprio(1);
-      gemm(kread, vread, qk_tag, pv_tag);
+      gemm_sk();
       __builtin_amdgcn_s_setprio(0);
-      if (k < N) softmax(N - 1 - k);
+      if (k < N && !sk_q) softmax(N - 1 - k);
     } else {
-      if (k >= 1) softmax(N - k);
+      if (k >= 1 && !sk_p) softmax(N - k);
       __builtin_amdgcn_s_setprio(1);
-      gemm(kread, vread, qk_tag, pv_tag);
+      gemm_sk();
       __builtin_amdgcn_s_setprio(0);
     }
   };
@@ -921,13 +954,26 @@ void fa_fwd_bf16_pp_kernel(Params p) {
     const char *kr, *vr;
     char *kd, *vd;
     bufs(0, kr, vr, kd, vd);
-    step(0, kr, vr, kd, vd, BoolTag<true>{}, BoolTag<false>{});
-    for (int k = 1; k < N; ++k) {
+    if (CAUSAL && ks > 0)
+      step(0, kr, vr, kd, vd, BoolTag<true>{}, BoolTag<false>{}, BoolTag<true>{});
+    else
+      step(0, kr, vr, kd, vd, BoolTag<true>{}, BoolTag<false>{}, BoolTag<false>{});
+    int k = 1;
+    if (CAUSAL) {
+      for (; k < min(N, ks); ++k) {
+        bufs(k, kr, vr, kd, vd);
+        step(k, kr, vr, kd, vd, BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
+      }
+    }
+    for (; k < N; ++k) {
       bufs(k, kr, vr, kd, vd);
-      step(k, kr, vr, kd, vd, BoolTag<true>{}, BoolTag<true>{});
+      step(k, kr, vr, kd, vd, BoolTag<true>{}, BoolTag<true>{}, BoolTag<false>{});
     }
     bufs(N, kr, vr, kd, vd);
-    step(N, kr, vr, kd, vd, BoolTag<false>{}, BoolTag<true>{});
+    if (CAUSAL && ks > N)
+      step(N, kr, vr, kd, vd, BoolTag<false>{}, BoolTag<true>{}, BoolTag<true>{});
+    else
+      step(N, kr, vr, kd, vd, BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
   }
 
   // ---- epilogue
