@@ -183,11 +183,11 @@ typedef struct fa_plan {
   int wg_per_cu;         /* resident workgroups per CU (LDS and VGPR limits)  */
   int vgprs_per_lane;    /* VGPR+AGPR budget per lane the kernel is built for */
   int64_t num_workgroups;/* grid size                                         */
-  int m_tiles;           /* query tiles per (sequence, head)                  */
+  int m_tiles;           /* query tiles (tile_m rows) per (sequence, head)    */
   int kernel_variant;    /* index of the compiled kernel                      */
-  int query_tiles;       /* 32-row query tiles per wave (tile_m = 128 * this) */
+  int query_tiles;       /* 32-row query tiles per wave                       */
   int heads_per_workgroup; /* query heads sharing one workgroup's K/V staging  */
-  int schedule;          /* 1, 2 or 3 (see fa_fwd_plan)                       */
+  int schedule;          /* 1, 2, 3 or 4 (see fa_fwd_plan)                    */
 } fa_plan_t;
 
 /*
