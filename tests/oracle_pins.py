@@ -4,7 +4,7 @@ Each ``pin_*`` function raises AssertionError when the oracle disagrees with
 something the mathematics or a library routine fixes independently: exact
 decoders checked against torch's dtype casts over every bit pattern, closed
 forms (two-key softmax, constant V, single admissible key), invariants (rows
-of P sum to one, key shift, key permutation), special cases that reduce to
+of P sum to one, key shift, key permutation, key repetition), special cases that reduce to
 ``torch.nn.functional.scaled_dot_product_attention`` in float64, and an
 independent one-pass online-softmax brute force (``oracle/online.py``).
 
@@ -175,6 +175,19 @@ def pin_key_permutation_invariance():
     o2, l2 = _run(w)
     _close(o2, o1, 1e-13, "key permutation O")
     _close(l2, l1, 1e-13, "key permutation LSE")
+
+
+def pin_key_repetition():
+    """Every key (with its value) present r times: each weight's numerator and the sum gain the
+    factor r, so O is unchanged and LSE grows by ln r (the GPU maximum-size tests rely on it)."""
+    w = fa_inputs.make(1, 2, 1, 6, 13, 8, causal=False, seed=17)
+    o1, l1 = _run(w)
+    r = 5
+    w.k, w.v = w.k.repeat(r, 1, 1).contiguous(), w.v.repeat(r, 1, 1).contiguous()
+    w.seqlen_k *= r
+    o2, l2 = _run(w)
+    _close(o2, o1, 1e-13, "key repetition O")
+    _close(l2, l1 + math.log(r), 1e-13, "key repetition LSE")
 
 
 # ----------------------------------------------------- library special cases

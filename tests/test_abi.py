@@ -75,6 +75,12 @@ def call(**kw):
     (dict(head_dim=256, head_dim_v=256), fa.FA_ERR_UNSUPPORTED),
     (dict(head_dim=128, head_dim_v=64), fa.FA_ERR_UNSUPPORTED),
     (dict(head_dim=0), fa.FA_ERR_INVALID),
+    # one sequence's K (or V) must stay below 2 GiB: bf16, 2 KV heads x 128 x 2 B per key
+    (dict(seqlen_k=(1 << 31) // (2 * 128 * 2)), fa.FA_ERR_UNSUPPORTED),
+    # fp8: one byte per element, so twice the keys
+    (dict(seqlen_k=(1 << 31) // (2 * 128), descales=P), fa.FA_ERR_UNSUPPORTED),
+    # fixed-length row offsets are 32-bit
+    (dict(batch=2, seqlen_q=1 << 30), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_validation_before_any_hip_call(kw, code):
     assert call(**kw) == code

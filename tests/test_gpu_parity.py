@@ -498,3 +498,58 @@ def test_graph_capture_replays(case):
         assert torch.isfinite(junk)
         assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), f"replay {rep}: O differs"
         assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32)), f"replay {rep}: LSE differs"
+
+
+# ----------------------------------------------------------------- maximum sizes
+
+def _repeat_keys(w, reps):
+    """K and V of ``w`` (one sequence of P keys) repeated ``reps`` times along the keys, on
+    the GPU.  Every key then occurs reps times with the same score, so the softmax weights
+    are those over the P keys: O is unchanged and LSE grows by exactly ln(reps)."""
+    return (w.k.to("cuda").repeat(reps, 1, 1).contiguous(),
+            w.v.to("cuda").repeat(reps, 1, 1).contiguous())
+
+
+@pytest.mark.parametrize("sq,causal", [(64, False), (1, True)])
+def test_longest_supported_key_range(sq, causal, schedule):
+    """One sequence whose K (and V) is just under the 2 GiB the kernels address per sequence:
+    1 KV head, D = 128, bf16, 1021 x 8216 = 8 388 536 keys (the largest multiple of the
+    1021-key period below 2^31 / 256).  The reference is the oracle over the 1021 keys, with
+    LSE + ln(8216); causal with one query row (bottom-right) sees every key."""
+    import exact_attention_forward_fa_amd as fa
+
+    period, reps = 1021, 8216
+    assert period * reps * 128 * 2 < (1 << 31) <= period * (reps + 1) * 128 * 2
+    w = fa_inputs.make(1, 2, 1, sq, period, 128, causal=False, seed=70 + sq,
+                       name=f"keys_{period}x{reps}_sq{sq}_c{int(causal)}_s{schedule}")
+    ro, rl = oracle_full(w)
+    q = w.q.to("cuda")
+    k, v = _repeat_keys(w, reps)
+    say(f"[gpu] fa_fwd {w.name}: hq=2 hkv=1 sq={sq} sk={period * reps} d=128 causal={causal}")
+    o, lse = fa.forward(q, k, v, causal=causal, softmax_scale=w.softmax_scale,
+                        max_seqlen_q=sq, max_seqlen_k=period * reps, batch=1)
+    torch.cuda.synchronize()
+    del k, v
+    compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro,
+            rl + np.log(reps), "bf16", w.name)
+
+
+def test_fp8_longest_supported_key_range():
+    """As above for e4m3 (one byte per element): 1021 x 16 432 = 16 777 072 keys."""
+    import exact_attention_forward_fa_amd as fa
+
+    period, reps = 1021, 16432
+    assert period * reps * 128 < (1 << 31) <= period * (reps + 1) * 128
+    w = fa_inputs.make(1, 2, 1, 64, period, 128, causal=False, seed=72, dtype="e4m3",
+                       name=f"fp8_keys_{period}x{reps}")
+    ro, rl = oracle_full(w)
+    q = w.q.to("cuda")
+    k, v = _repeat_keys(w, reps)
+    ds = torch.from_numpy(w.descales).to("cuda")
+    say(f"[gpu] fa_fwd {w.name}: hq=2 hkv=1 sq=64 sk={period * reps} d=128 fp8")
+    o, lse = fa.forward(q, k, v, causal=False, softmax_scale=w.softmax_scale,
+                        max_seqlen_q=64, max_seqlen_k=period * reps, descales=ds, batch=1)
+    torch.cuda.synchronize()
+    del k, v
+    compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro,
+            rl + np.log(reps), "e4m3", w.name)
