@@ -221,6 +221,83 @@ def run_kvcache(args, cfg) -> int:
     return 0
 
 
+# The five configurations of the metric (the dense MHA one run causal and not); each gets its
+# own entry in the "configs" list of the output line, timed like the headline workload.
+CONFIG_WORKLOADS = ["tiny_b1_h2_s256_d64", "mha_b4_h16_s1024_d128", "mha_causal_b4_h16_s1024_d128",
+                    "gqa_causal_b2_hq32_hkv8_s8192_d128", "varlen_causal_18seq_h16_d128",
+                    "fp8_causal_b1_h32_s16384_d128"]
+
+
+def device_inputs(w):
+    import torch
+
+    q, k, v = w.q.cuda(), w.k.cuda(), w.v.cuda()
+    cu = torch.from_numpy(w.cu_seqlens).cuda() if w.cu_seqlens is not None else None
+    ds = torch.from_numpy(w.descales).cuda() if w.descales is not None else None
+    o = torch.empty((w.total_q, w.heads_q, w.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device="cuda")
+    return q, k, v, cu, ds, o, lse
+
+
+def timed_launches(w, tensors, warmup: int, steps: int):
+    """Launch fa_fwd warmup + steps times back to back on torch's current stream; returns
+    (kernel ms per launch from HIP events recorded on that stream, wall ms per launch)."""
+    import torch
+
+    import exact_attention_forward_fa_amd as fa
+
+    q, k, v, cu, ds, o, lse = tensors
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fa_fwd(q, k, v, o, lse, w.batch, w.heads_q, w.heads_kv, w.seqlen_q, w.seqlen_k, cu,
+                  w.head_dim, w.head_dim_v, w.softmax_scale, int(w.causal), ds,
+                  stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall * 1e3 / steps
+
+
+def config_lines(warmup: int, steps: int):
+    """Every configuration of the metric: kernel time per launch (HIP events), TFLOPS and the
+    fraction of its input type's dense MFMA peak, and the schedule the planner chose."""
+    import torch
+
+    import fa_inputs
+    import exact_attention_forward_fa_amd as fa
+
+    out = []
+    for name in CONFIG_WORKLOADS:
+        w = fa_inputs.workload(name)
+        tensors = device_inputs(w)
+        kernel_ms, _ = timed_launches(w, tensors, warmup, steps)
+        flops = workload_flops(w)
+        peak = PEAK_TFLOPS[w.dtype]
+        tf = flops / (kernel_ms * 1e-3) / 1e12
+        plan = fa.fa_fwd_plan(fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_E4M3,
+                              w.batch, w.heads_q, w.heads_kv, w.seqlen_q, w.seqlen_k,
+                              w.cu_seqlens is not None, w.head_dim, w.head_dim_v, w.causal)
+        line = {"workload": name, "dtype": w.dtype, "causal": w.causal, "flops": flops,
+                "kernel_ms": round(kernel_ms, 5), "tflops": round(tf, 2), "peak": peak,
+                "frac": round(tf / peak, 4), "schedule": int(plan.schedule)}
+        log(f"config {name}: {kernel_ms:.4f} ms, {tf:.1f} TFLOPS = {100 * tf / peak:.1f}% of "
+            f"{peak:.0f} (schedule {plan.schedule})")
+        out.append(line)
+        del tensors
+        torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +307,10 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration lines (all five configurations of the metric)")
+    ap.add_argument("--config-steps", type=int, default=100,
+                    help="timed launches per configuration line (after as many warm-up launches)")
     ap.add_argument("--exp2-offload", type=int, default=0, choices=[0, 4, 8],
                     help="ping-pong schedule: every N-th exponential on the FMA polynomial "
                          "(0: off, the default)")
@@ -261,37 +342,19 @@ def main(argv=None) -> int:
     fa.fa_set_exp2_offload(args.exp2_offload)
     log(f"workload {w.name}: batch={w.batch} hq={w.heads_q} hkv={w.heads_kv} sq={w.seqlen_q} "
         f"sk={w.seqlen_k} d={w.head_dim} causal={w.causal} dtype={w.dtype}")
-    q, k, v = w.q.cuda(), w.k.cuda(), w.v.cuda()
-    cu = torch.from_numpy(w.cu_seqlens).cuda() if w.cu_seqlens is not None else None
-    ds = torch.from_numpy(w.descales).cuda() if w.descales is not None else None
-    o = torch.empty((w.total_q, w.heads_q, w.head_dim_v), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step():
-        fa.fa_fwd(q, k, v, o, lse, w.batch, w.heads_q, w.heads_kv, w.seqlen_q, w.seqlen_k, cu,
-                  w.head_dim, w.head_dim_v, w.softmax_scale, int(w.causal), ds,
-                  stream=stream.cuda_stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    tensors = device_inputs(w)
+    kernel_ms, ms_per_step = timed_launches(w, tensors, args.warmup, args.steps)
+    del tensors
     flops = workload_flops(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log(f"kernel {kernel_ms:.4f} ms/launch (events), wall {ms_per_step:.4f} ms/step, "
         f"{achieved:.1f} TFLOPS = {100 * achieved / peak:.1f}% of {peak:.0f}")
+
+    configs = None
+    if not args.no_configs:
+        configs = config_lines(args.config_steps, args.config_steps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -322,6 +385,7 @@ def main(argv=None) -> int:
                      "traffic": None if args.exp2_offload else load_traffic(w.name),
                      "kernel_ms": round(kernel_ms, 5)},
         "cpu_baseline": cpu,
+        "configs": configs,
     }
     if args.exp2_offload:
         line["config"]["exp2_offload"] = args.exp2_offload
