@@ -89,6 +89,8 @@ def _load():
     lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                    i32, i32, ctypes.c_float, i32, vp, vp]
     lib.fa_fwd_kvcache.restype = i32
+    lib.fa_check_cu_seqlens.argtypes = [vp, i32, i32, i32, ctypes.c_int64, ctypes.c_int64]
+    lib.fa_check_cu_seqlens.restype = i32
     return lib
 
 
@@ -149,6 +151,24 @@ def fa_fwd_plan(dtype: int, batch: int, heads_q: int, heads_kv: int, seqlen_q: i
     return out
 
 
+def fa_check_cu_seqlens(cu_host, batch: int, seqlen_q: int, seqlen_k: int, rows_q: int,
+                        rows_k: int) -> None:
+    """Check a host copy of a packed batch's offsets (int32[2*(batch+1)], numpy or CPU tensor)
+    with the library's host-side validator; raises FaError(FA_ERR_INVALID) when the offsets
+    do not start at 0, decrease, exceed the maxima or do not match the tensors' row counts."""
+    import numpy as np
+
+    if hasattr(cu_host, "detach"):
+        cu_host = cu_host.detach().cpu().numpy()
+    arr = np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+    if arr.ndim != 1 or arr.shape[0] != 2 * (int(batch) + 1):
+        raise FaError(FA_ERR_INVALID, "fa_check_cu_seqlens")
+    rc = _lib.fa_check_cu_seqlens(arr.ctypes.data_as(ctypes.c_void_p), int(batch), int(seqlen_q),
+                                  int(seqlen_k), int(rows_q), int(rows_k))
+    if rc:
+        raise FaError(rc, "fa_check_cu_seqlens")
+
+
 def _ptr(x) -> Optional[int]:
     """A device pointer from a torch tensor, an int address, or None."""
     if x is None:
@@ -187,7 +207,10 @@ def forward(q, k, v, *, causal: bool, softmax_scale: Optional[float] = None, cu_
     q [total_q, Hq, D], k [total_k, Hkv, D], v [total_k, Hkv, Dv] on the GPU: bf16, or uint8 /
     float8_e4m3fn codes with ``descales`` (float32[3] on the GPU).  Without ``cu_seqlens`` the
     leading dimension is batch*seqlen with ``batch`` given (default 1).  With ``cu_seqlens``
-    (int32[2*(batch+1)] on the GPU) ``max_seqlen_q`` / ``max_seqlen_k`` must be given.
+    (int32[2*(batch+1)] on the GPU) ``max_seqlen_q`` / ``max_seqlen_k`` must be given; a host copy
+    of the offsets is checked first (fa_check_cu_seqlens: starting at 0, non-decreasing, lengths
+    within the maxima, cu[batch] == q.shape[0], cu[2*batch+1] <= k.shape[0]), which costs one
+    device-to-host copy per call.  ``out`` / ``lse`` may be given (shapes as returned).
     Returns (O [total_q, Hq, Dv], LSE [Hq, total_q]).
     """
     import torch
@@ -201,31 +224,44 @@ def forward(q, k, v, *, causal: bool, softmax_scale: Optional[float] = None, cu_
         if t.dtype not in want:
             raise ValueError(f"{name} has dtype {t.dtype}, expected one of {want}")
     total_q, hq, d = q.shape
-    total_k, hkv, _ = k.shape
+    total_k, hkv, dk = k.shape
     dv = v.shape[2]
+    if dk != d or v.shape[0] != total_k or v.shape[1] != hkv:
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
     if cu_seqlens is not None:
         if max_seqlen_q is None or max_seqlen_k is None:
             raise ValueError("cu_seqlens needs max_seqlen_q and max_seqlen_k")
-        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.numel() % 2:
-            raise ValueError("cu_seqlens must be int32[2*(batch+1)] on the GPU")
+        if (cu_seqlens.dtype != torch.int32 or cu_seqlens.device != q.device
+                or cu_seqlens.numel() % 2 or cu_seqlens.numel() < 4):
+            raise ValueError("cu_seqlens must be int32[2*(batch+1)] on the device of q")
         nb = cu_seqlens.numel() // 2 - 1
         if batch is not None and batch != nb:
             raise ValueError("batch does not match cu_seqlens")
         batch, sq, sk = nb, int(max_seqlen_q), int(max_seqlen_k)
+        # the kernels read the offsets on the device only; check a host copy of them first
+        fa_check_cu_seqlens(cu_seqlens, batch, sq, sk, total_q, total_k)
     else:
         batch = 1 if batch is None else int(batch)
-        if total_q % batch or total_k % batch:
+        if batch <= 0 or total_q % batch or total_k % batch:
             raise ValueError("leading dimensions are not divisible by batch")
         sq, sk = total_q // batch, total_k // batch
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    if descales is not None and (not descales.is_cuda or descales.dtype != torch.float32
+    if descales is not None and (descales.device != q.device or descales.dtype != torch.float32
                                  or descales.numel() != 3):
-        raise ValueError("descales must be float32[3] on the GPU")
+        raise ValueError("descales must be float32[3] on the device of q")
     if out is None:
         out = torch.empty((total_q, hq, dv), dtype=torch.bfloat16, device=q.device)
+    elif (out.shape != (total_q, hq, dv) or out.dtype != torch.bfloat16 or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError(f"out must be a contiguous bf16 tensor of shape {(total_q, hq, dv)}")
     if lse is None:
         lse = torch.empty((hq, total_q), dtype=torch.float32, device=q.device)
+    elif (lse.shape != (hq, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.device != q.device):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(hq, total_q)}")
     fa_fwd(q, k, v, out, lse, batch, hq, hkv, sq, sk, cu_seqlens, d, dv, softmax_scale,
            int(bool(causal)), descales)
     return out, lse
@@ -271,15 +307,32 @@ def forward_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, 
             raise ValueError(f"{name} has dtype {t.dtype}, expected one of {want}")
     b, sq, hq, d = q.shape
     _, cap, hkv, _ = k_cache.shape
+    if k_cache.shape != (b, cap, hkv, d) or v_cache.shape != (b, cap, hkv, d):
+        raise ValueError(f"caches must be [batch, capacity, heads_kv, head_dim] = {(b, cap, hkv, d)}")
     snew = 0 if k_new is None else k_new.shape[1]
-    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda or cache_seqlens.numel() != b:
-        raise ValueError("cache_seqlens must be int32[batch] on the GPU")
+    if k_new is not None and (k_new.shape != (b, snew, hkv, d) or v_new.shape != (b, snew, hkv, d)):
+        raise ValueError(f"new rows must be [batch, seqlen_new, heads_kv, head_dim] = {(b, snew, hkv, d)}")
+    for name, t in tensors:
+        if t.device != q.device:
+            raise ValueError(f"{name} is not on the device of q")
+    if (cache_seqlens.dtype != torch.int32 or cache_seqlens.device != q.device
+            or cache_seqlens.numel() != b):
+        raise ValueError("cache_seqlens must be int32[batch] on the device of q")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
+    if descales is not None and (descales.device != q.device or descales.dtype != torch.float32
+                                 or descales.numel() != 3):
+        raise ValueError("descales must be float32[3] on the device of q")
     if out is None:
         out = torch.empty((b * sq, hq, d), dtype=torch.bfloat16, device=q.device)
+    elif (out.shape != (b * sq, hq, d) or out.dtype != torch.bfloat16 or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError(f"out must be a contiguous bf16 tensor of shape {(b * sq, hq, d)}")
     if lse is None:
         lse = torch.empty((hq, b * sq), dtype=torch.float32, device=q.device)
+    elif (lse.shape != (hq, b * sq) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.device != q.device):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(hq, b * sq)}")
     fa_fwd_kvcache(q, k_cache, v_cache, k_new, v_new, out, lse, b, hq, hkv, sq, snew, cap,
                    cache_seqlens, d, d, softmax_scale, int(bool(causal)), descales)
     return out, lse

@@ -52,6 +52,20 @@ const char* fa_strerror(int code) {
   }
 }
 
+int fa_check_cu_seqlens(const int* cu, int batch, int seqlen_q, int seqlen_k, int64_t rows_q,
+                        int64_t rows_k) {
+  if (!cu) return FA_ERR_NULL;
+  if (batch <= 0 || seqlen_q < 0 || seqlen_k < 0 || rows_q < 0 || rows_k < 0) return FA_ERR_INVALID;
+  const int* ck = cu + batch + 1;
+  if (cu[0] != 0 || ck[0] != 0) return FA_ERR_INVALID;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t lq = (int64_t)cu[b + 1] - cu[b], lk = (int64_t)ck[b + 1] - ck[b];
+    if (lq < 0 || lq > seqlen_q || lk < 0 || lk > seqlen_k) return FA_ERR_INVALID;
+  }
+  if (cu[batch] != rows_q || ck[batch] > rows_k) return FA_ERR_INVALID;
+  return FA_OK;
+}
+
 int fa_set_schedule(int schedule) {
   if (schedule < 0 || schedule > 4) return FA_ERR_INVALID;
   g_schedule.store(schedule, std::memory_order_relaxed);

@@ -29,10 +29,14 @@
  *   cu_seqlens == NULL: total_q = batch*seqlen_q, total_k = batch*seqlen_k.
  *   cu_seqlens != NULL: int32[2*(batch+1)]; cu_seqlens[0..batch] are the
  *     query offsets, cu_seqlens[batch+1 .. 2*batch+1] the key offsets of a
- *     packed batch; seqlen_q / seqlen_k are then the largest sequence
- *     lengths (they size the launch grid).  Offsets must be non-decreasing,
- *     start at 0 and every length must be <= the maximum passed: this is the
- *     caller's contract and is not checked on the device.
+ *     packed batch (the page's SeqlenInfo: per-sequence offsets and
+ *     lengths); total_q = cu_seqlens[batch], total_k = cu_seqlens[2*batch+1]
+ *     (LSE rows are total_q long); seqlen_q / seqlen_k are then the largest
+ *     sequence lengths (they size the launch grid).  Offsets must be
+ *     non-decreasing, start at 0 and every length must be <= the maximum
+ *     passed: the array lives on the device, where fa_fwd does not read it
+ *     on the host, so this is the caller's contract -- fa_check_cu_seqlens
+ *     checks a host copy of it (the Python binding always does).
  *
  * Ownership: every pointer belongs to the caller; the library allocates no
  * device memory and keeps no per-call state (it caches one device-property
@@ -92,10 +96,32 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int head_dim, int head_dim_v, float softmax_scale, int causal, const float* descales,
            void* stream);
 
-/* Text for a return code (static storage, never NULL). */
+/* Text for a return code (static storage, never NULL).  FA_ERR_UNSUPPORTED
+ * is the answer of the tile screen ("FlashAttention on SM120 reusing the SM80
+ * forward", section on can_implement: a configuration whose buffers do not
+ * fit is refused before launch); rows without an admissible key are not an
+ * error but the epilogue's store_zero case ("FlashAttention core algorithm:
+ * forward pass", epilogue). */
 const char* fa_strerror(int code);
 
-/* ---- tile / occupancy screening (pure host functions) ------------------ */
+/*
+ * fa_check_cu_seqlens -- host-side check of a packed batch's offsets (the
+ * contract stated with the layouts above), on a HOST copy of the int32
+ * array of 2*(batch+1) entries:
+ *   cu[0] == 0 and cu[batch+1] == 0; both halves non-decreasing;
+ *   every query length cu[b+1]-cu[b] <= seqlen_q, every key length
+ *   cu[batch+2+b]-cu[batch+1+b] <= seqlen_k;
+ *   cu[batch] == rows_q (the rows of Q, O and of each LSE row) and
+ *   cu[2*batch+1] <= rows_k (the rows of K and V).
+ * Pure host function.  Returns FA_OK, FA_ERR_NULL (cu_host NULL) or
+ * FA_ERR_INVALID (batch <= 0, negative sizes, or a violated condition).
+ * A call that passes this check cannot make fa_fwd read or write outside
+ * Q/K/V/O/LSE buffers of those row counts.
+ */
+int fa_check_cu_seqlens(const int* cu_host, int batch, int seqlen_q, int seqlen_k,
+                        int64_t rows_q, int64_t rows_k);
+
+/* ---- KV cache ------------------------------------------------------------ */
 
 /*
  * fa_fwd_kvcache -- append new keys/values to a KV cache, then run the
@@ -131,6 +157,8 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const void* k_ne
                    int seqlen_q, int seqlen_new, int cache_capacity, const int* cache_seqlens,
                    int head_dim, int head_dim_v, float softmax_scale, int causal,
                    const float* descales, void* stream);
+
+/* ---- tile / occupancy screening (host functions) -------------------------- */
 
 /*
  * Capacity figures of a device, as the shared-memory screen of "FlashAttention
@@ -191,8 +219,13 @@ typedef struct fa_plan {
 } fa_plan_t;
 
 /*
- * fa_fwd_plan -- choose the kernel configuration for a shape (pure host
- * function, no HIP call).  dev == NULL means gfx950.  Returns FA_OK,
+ * fa_fwd_plan -- choose the kernel configuration for a shape: the
+ * can_implement screen of "FlashAttention on SM120 reusing the SM80 forward"
+ * (buffers against the per-block and per-CU shared-memory capacity, blocks per
+ * CU) carried on to gfx950's LDS and register file, plus the choice of
+ * schedule.  Host function, no HIP call; its inputs are the arguments and the
+ * process-wide schedule override of fa_set_schedule (0, the default, leaves
+ * the choice to the rules below).  dev == NULL means gfx950.  Returns FA_OK,
  * FA_ERR_NULL, FA_ERR_INVALID or FA_ERR_UNSUPPORTED (nothing fits `dev`).
  *
  * Schedules:

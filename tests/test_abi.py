@@ -324,3 +324,77 @@ def test_one_hip_runtime_when_package_is_imported_before_torch():
                        cwd=ROOT)
     assert r.returncode == 0, r.stderr
     assert r.stdout.split()[0] == "1", r.stdout
+
+
+# ---------------------------------------------------------------- cu_seqlens validator
+
+def _cu(q_lens, k_lens):
+    import numpy as np
+
+    return np.concatenate([np.concatenate([[0], np.cumsum(q_lens)]),
+                           np.concatenate([[0], np.cumsum(k_lens)])]).astype(np.int32)
+
+
+def check_cu(cu, batch, sq, sk, rows_q, rows_k):
+    try:
+        fa.fa_check_cu_seqlens(cu, batch, sq, sk, rows_q, rows_k)
+        return fa.FA_OK
+    except fa.FaError as e:
+        return e.code
+
+
+def test_cu_seqlens_validator_accepts_packed_batches():
+    cu = _cu([300, 1, 0, 129], [517, 64, 40, 0])
+    assert check_cu(cu, 4, 300, 517, 430, 621) == fa.FA_OK
+    assert check_cu(cu, 4, 300, 517, 430, 10_000) == fa.FA_OK  # K/V may be longer than used
+    # the named varlen workload's offsets
+    import fa_inputs
+
+    lens = fa_inputs.varlen_lengths(4)
+    cu = _cu([a for a, _ in lens], [b for _, b in lens])
+    assert check_cu(cu, len(lens), max(a for a, _ in lens), max(b for _, b in lens),
+                    int(cu[len(lens)]), int(cu[-1])) == fa.FA_OK
+
+
+@pytest.mark.parametrize("case", ["q_start", "k_start", "q_decreasing", "k_decreasing", "q_over_max",
+                                  "k_over_max", "rows_q_short", "rows_q_long", "rows_k_short",
+                                  "wrong_length", "batch0"])
+def test_cu_seqlens_validator_rejects(case):
+    """Every condition of the contract has its own rejection (FA_ERR_INVALID), before anything is
+    launched: offsets that do not start at 0, that decrease, lengths above the maxima, and a
+    total that does not match the rows of Q (and of each LSE row) or exceeds the rows of K/V."""
+    base = _cu([100, 50, 7], [120, 60, 7])
+    cu, batch, sq, sk, rq, rk = base.copy(), 3, 100, 120, 157, 187
+    if case == "q_start":
+        cu[:4] += 1
+        rq += 1
+    elif case == "k_start":
+        cu[4:] += 1
+        rk += 1
+    elif case == "q_decreasing":
+        cu[2] = cu[1] - 1
+    elif case == "k_decreasing":
+        cu[6] = cu[5] - 1
+    elif case == "q_over_max":
+        sq = 99
+    elif case == "k_over_max":
+        sk = 119
+    elif case == "rows_q_short":
+        rq = 156
+    elif case == "rows_q_long":
+        rq = 158  # LSE rows are cu[batch] long: a padded q would stride LSE wrongly
+    elif case == "rows_k_short":
+        rk = 186
+    elif case == "wrong_length":
+        cu = cu[:-1]
+    elif case == "batch0":
+        batch = 0
+        cu = cu[:2]
+    assert check_cu(cu, batch, sq, sk, rq, rk) == fa.FA_ERR_INVALID
+
+
+def test_cu_seqlens_validator_null():
+    lib = ctypes.CDLL(fa.library_path())
+    lib.fa_check_cu_seqlens.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int64, ctypes.c_int64]
+    assert lib.fa_check_cu_seqlens(None, 1, 1, 1, 1, 1) == fa.FA_ERR_NULL
