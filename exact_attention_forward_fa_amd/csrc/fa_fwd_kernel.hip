@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include "../../include/fa_fwd.h"
+#include "fa_exp2_poly.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -52,24 +53,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// 2^x on the FMA pipe instead of the transcendental unit -- the polynomial
-// replacement of the exponential that "Dissecting the SM_120
-// Microarchitecture" lists first among the remedies for the softmax-bound
-// FlashAttention tile (section 11.2, Fig. 12).  Cody-Waite split x = n + f
-// with n = rint(x), f in [-1/2, 1/2]; 2^f by a degree-3 polynomial fitted here
-// by iterated weighted least squares for relative error on [-1/2, 1/2] (max
-// 7.5e-5, below the bf16 rounding of P); 2^n by ldexp.  x is clamped at -160,
-// so a masked score (-inf) gives exactly 0; NaN propagates.
-__device__ __forceinline__ float exp2_poly(float x) {
-  x = __builtin_elementwise_maximum(x, -160.f);
-  const float n = __builtin_rintf(x);
-  const float f = x - n;
-  float p = __builtin_fmaf(0.05517605319619179f, f, 0.24261149764060974f);
-  p = __builtin_fmaf(p, f, 0.6932601928710938f);
-  p = __builtin_fmaf(p, f, 0.9999280571937561f);
-  return __builtin_ldexpf(p, (int)n);
-}
 
 // Maximum that propagates NaN (IEEE 754-2019 maximum).  Scores are never NaN
 // here; unlike fmaxf it needs no quieting of its inputs, and chains of it map
@@ -1252,6 +1235,13 @@ void fa_fwd_bf16_decode_kernel(Params p) {
 //  * O^T += V^T P^T with P quantised to e4m3 (P <= 2^kLazy < 448); V^T
 //    arrives through ds_read_b64_tr_b8, which hands lane i of each 16-lane
 //    group column i of an 8-row x 16-byte block.
+//  * O is normalised by the sum of the quantised weights that multiplied V,
+//    taken on the matrix core as one more tile of the same product with an
+//    all-ones A operand (every row of it is the column sum of P^T); the LSE
+//    keeps the fp32 sum of the unquantised P.  With P taken against a stale
+//    maximum even the largest weight of a row is rounded (3 mantissa bits),
+//    and normalising by the unquantised sum would scale O by that rounding
+//    (measured 7.9e-2 on rows spread over a few keys, against 3e-2 this way).
 //  * The q and k descales fold into the exp2 scale (the forward-pass page's
 //    FP8 branch multiplies softmax_scale_log2 by q_descale * k_descale); the
 //    v descale multiplies O in the epilogue.
@@ -1282,6 +1272,10 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   // format 0 (e4m3) for both operands, E8M0 block scales 127 = 2^0
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+
+// Four e4m3 ones (0x38 = 1.0) per dword: the A operand whose product with P^T
+// is the column sum of P^T in every row.
+constexpr int kE4m3OnesWord = 0x38383838;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1421,6 +1415,10 @@ void fa_fwd_fp8_kernel(Params p) {
   f32x16 oacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  // lq: the sum of the e4m3 weights that multiplied V (all 16 registers alike)
+  f32x16 lq = f32x16{};
+  const i32x8 ones = {kE4m3OnesWord, kE4m3OnesWord, kE4m3OnesWord, kE4m3OnesWord,
+                      kE4m3OnesWord, kE4m3OnesWord, kE4m3OnesWord, kE4m3OnesWord};
   float m_run = -INFINITY;
   float l_run = 0.f;
 
@@ -1490,6 +1488,7 @@ void fa_fwd_fp8_kernel(Params p) {
         const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
         m_run = m_new;
         l_run *= alpha;
+        lq *= alpha;
 #pragma unroll
         for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
       }
@@ -1512,6 +1511,7 @@ void fa_fwd_fp8_kernel(Params p) {
     }
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[t] = mfma_fp8(va_op[t], pb, oacc[t]);
+    lq = mfma_fp8(ones, pb, lq);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
   char* const k0b = kbuf0;
@@ -1538,8 +1538,13 @@ void fa_fwd_fp8_kernel(Params p) {
   }
 
   pin_accumulators(oacc);
+  {
+    f32x16 lqa[1] = {lq};
+    pin_accumulators(lqa);
+    lq = lqa[0];
+  }
   const float l_tot = halfwave_sum(l_run);
-  const float inv = l_tot > 0.f ? dvs / l_tot : 0.f;
+  const float inv = l_tot > 0.f && lq[0] > 0.f ? dvs / lq[0] : 0.f;
   store_o_rows<DT>(oacc, inv, O + qrow, hf, qvalid);
   if (qvalid && hf == 0)
     p.lse[lse_idx] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;

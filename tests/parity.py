@@ -27,18 +27,56 @@ def to_device(w: fa_inputs.Workload):
     return q, k, v, cu, ds
 
 
+def nan_outputs(w: fa_inputs.Workload):
+    """O and LSE buffers pre-filled with NaN, so that an element the kernel never writes cannot
+    pass any check (every comparison below rejects NaN)."""
+    o = torch.full((w.total_q, w.heads_q, w.head_dim_v), float("nan"), dtype=torch.bfloat16,
+                   device="cuda")
+    lse = torch.full((w.heads_q, w.total_q), float("nan"), dtype=torch.float32, device="cuda")
+    return o, lse
+
+
 def gpu_run(w: fa_inputs.Workload, tensors=None):
-    """Forward on the GPU through the C ABI.  Returns (O [total_q,Hq,Dv], LSE [Hq,total_q]) float64."""
+    """Forward on the GPU through the C ABI, into NaN-filled outputs.
+    Returns (O [total_q,Hq,Dv], LSE [Hq,total_q]) as float64."""
     import exact_attention_forward_fa_amd as fa
 
     q, k, v, cu, ds = tensors if tensors is not None else to_device(w)
     say(f"[gpu] fa_fwd {w.name}: b={w.batch} hq={w.heads_q} hkv={w.heads_kv} sq={w.seqlen_q} "
         f"sk={w.seqlen_k} d={w.head_dim} causal={w.causal} dtype={w.dtype} seed={w.seed}")
-    o, lse = fa.forward(q, k, v, causal=w.causal, softmax_scale=w.softmax_scale, cu_seqlens=cu,
-                        max_seqlen_q=w.seqlen_q, max_seqlen_k=w.seqlen_k, descales=ds,
-                        batch=w.batch)
+    o, lse = nan_outputs(w)
+    fa.forward(q, k, v, causal=w.causal, softmax_scale=w.softmax_scale, cu_seqlens=cu,
+               max_seqlen_q=w.seqlen_q, max_seqlen_k=w.seqlen_k, descales=ds, batch=w.batch,
+               out=o, lse=lse)
     torch.cuda.synchronize()
     return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def dead_rows(w: fa_inputs.Workload):
+    """Boolean [Hq, total_q]: rows with no admissible key (bottom-right causal: i < sq - sk;
+    any row of a sequence with no key), from the lengths alone."""
+    dead = np.zeros((w.heads_q, w.total_q), dtype=bool)
+    q0 = 0
+    for sq, sk in w.lengths:
+        n = sq if sk == 0 else (min(max(sq - sk, 0), sq) if w.causal else 0)
+        dead[:, q0:q0 + n] = True
+        q0 += sq
+    return dead
+
+
+def check_written(w: fa_inputs.Workload, o, lse):
+    """Whole-output checks that need no reference: every element written (no NaN left from the
+    pre-fill), every row with an admissible key has a finite LSE and a finite O, every row
+    without one is exactly O = 0 and LSE = -inf."""
+    dead = dead_rows(w)
+    assert not np.isnan(lse).any(), f"{w.name}: {int(np.isnan(lse).sum())} LSE elements not written"
+    assert not np.isnan(o).any(), f"{w.name}: {int(np.isnan(o).sum())} O elements not written"
+    assert np.all(lse[dead] == -np.inf), f"{w.name}: a fully masked row has LSE != -inf"
+    assert np.all(o[dead.T] == 0.0), f"{w.name}: a fully masked row has O != 0"
+    assert np.all(np.isfinite(lse[~dead])), f"{w.name}: non-finite LSE on a row with keys"
+    assert np.all(np.isfinite(o[~dead.T])), f"{w.name}: non-finite O on a row with keys"
+    say(f"[written] {w.name}: all {o.size} O and {lse.size} LSE elements written; "
+        f"{int(dead.sum())} fully masked rows exact")
 
 
 def oracle_full(w: fa_inputs.Workload):
@@ -96,6 +134,24 @@ def sample_rows(w: fa_inputs.Workload, n_random: int = 24, seed: int = 0):
         sq = w.lengths[b][0]
         if sq:
             rows.add((b, int(rng.integers(0, w.heads_q)), int(rng.integers(0, sq))))
+    return sorted(rows)
+
+
+def tile_rows(w: fa_inputs.Workload, tile: int = 128, slice_rows: int = 32, seed: int = 0):
+    """Rows (b, h, i) covering every (sequence, query head, 128-row query tile): the tile's
+    first row, its last row inside the sequence and one random row of each of its 32-row
+    slices (the rows one wave owns), so that every workgroup's and every wave's output is
+    compared with the oracle; plus the edge rows of sample_rows."""
+    rng = np.random.default_rng(seed)
+    rows = set(sample_rows(w, n_random=0, seed=seed))
+    for b, (sq, _) in enumerate(w.lengths):
+        for m0 in range(0, sq, tile):
+            last = min(m0 + tile, sq) - 1
+            for h in range(w.heads_q):
+                rows.add((b, h, m0))
+                rows.add((b, h, last))
+                for s0 in range(m0, last + 1, slice_rows):
+                    rows.add((b, h, int(rng.integers(s0, min(s0 + slice_rows, last + 1)))))
     return sorted(rows)
 
 

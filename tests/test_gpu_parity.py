@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import fa_inputs
-from parity import compare, gather_rows, gpu_run, oracle_full, oracle_rows, sample_rows, say, to_device
+from parity import (check_written, compare, gather_rows, gpu_run, nan_outputs, oracle_full,
+                    oracle_rows, say, tile_rows, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,14 +30,18 @@ def full_check(w):
     return compare(o, lse, ro, rl, w.dtype, w.name)
 
 
-def sampled_check(w, n_random=24):
+def sampled_check(w):
+    """Full-size workloads: the whole output is checked for unwritten elements (NaN pre-fill)
+    and exact fully masked rows, and rows of every (sequence, head, query tile, 32-row slice)
+    are compared with the oracle."""
     tensors = to_device(w)
     o, lse = gpu_run(w, tensors)
-    rows = sample_rows(w, n_random=n_random, seed=w.seed)
-    say(f"[oracle] {len(rows)} sampled rows of {w.name}")
+    check_written(w, o, lse)
+    rows = tile_rows(w, seed=w.seed)
+    say(f"[oracle] {len(rows)} rows of {w.name} (every tile and 32-row slice of every head)")
     ro, rl = oracle_rows(w, rows)
     og, lg = gather_rows(w, o, lse, rows)
-    compare(og, lg, ro, rl, w.dtype, w.name + " (sampled rows)")
+    compare(og, lg, ro, rl, w.dtype, w.name + " (rows of every tile)")
     return o, lse
 
 
@@ -52,9 +57,28 @@ def test_mha_1024(name, schedule):
 
 
 def test_gqa_causal_8192_sampled():
+    sampled_check(fa_inputs.workload("gqa_causal_b2_hq32_hkv8_s8192_d128"))
+
+
+@pytest.mark.timeout(900)
+def test_gqa_causal_8192_full_oracle():
+    """The bench workload in the launch configuration bench.py times, every output element
+    against the oracle (524 288 rows x 128 dims, about 1.1e12 fp64 flops: 1-2 minutes on the
+    host's cores), in chunks of 32 768 rows with a progress line each."""
     w = fa_inputs.workload("gqa_causal_b2_hq32_hkv8_s8192_d128")
-    o, lse = sampled_check(w, n_random=32)
-    assert np.isfinite(lse).all() and np.isfinite(o).all()
+    o, lse = gpu_run(w)
+    check_written(w, o, lse)
+    rows = np.array([(b, h, i) for b in range(w.batch) for h in range(w.heads_q)
+                     for i in range(w.seqlen_q)], dtype=np.int32)
+    eo = el = 0.0
+    chunk = 32768
+    for c0 in range(0, rows.shape[0], chunk):
+        part = rows[c0:c0 + chunk]
+        ro, rl = oracle_rows(w, part)
+        og, lg = gather_rows(w, o, lse, [tuple(r) for r in part])
+        a, b = compare(og, lg, ro, rl, w.dtype, f"{w.name} rows {c0}..{c0 + part.shape[0] - 1}")
+        eo, el = max(eo, a), max(el, b)
+    say(f"[parity] {w.name} whole output: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
 
 
 def test_gqa_causal_8192_sampled_one_tile_per_wave():
@@ -64,23 +88,17 @@ def test_gqa_causal_8192_sampled_one_tile_per_wave():
     w = fa_inputs.workload("gqa_causal_b2_hq32_hkv8_s8192_d128")
     fa.fa_set_schedule(1)
     try:
-        o, lse = sampled_check(w, n_random=16)
+        sampled_check(w)
     finally:
         fa.fa_set_schedule(0)
-    assert np.isfinite(lse).all() and np.isfinite(o).all()
 
 
 def test_varlen_causal_sampled():
+    """Every row that sees no key (sk < sq, i < sq - sk) exactly zero / -inf, every other row
+    written, rows of every tile against the oracle."""
     w = fa_inputs.workload("varlen_causal_18seq_h16_d128")
-    o, lse = sampled_check(w, n_random=32)
-    # every row that sees no key (sk < sq, i < sq - sk) is exactly zero / -inf
-    cu = w.cu_seqlens
-    for b, (sq, sk) in enumerate(w.lengths):
-        dead = max(sq - sk, 0)
-        q0 = int(cu[b])
-        assert np.all(lse[:, q0:q0 + dead] == -np.inf)
-        assert np.all(o[q0:q0 + dead] == 0.0)
-        assert np.all(np.isfinite(lse[:, q0 + dead:q0 + sq]))
+    assert any(sk < sq for sq, sk in w.lengths)
+    sampled_check(w)
 
 
 def test_varlen_equals_per_sequence_calls(schedule):
@@ -262,17 +280,41 @@ def test_running_max_growth(shape, causal, pattern, schedule):
     full_check(w)
 
 
+# The fp8 matrix instruction sums the products of the score's dot product to about 14 bits
+# relative to their magnitude (measured alike on the scaled f8f6f4 form the kernel uses and on
+# the unscaled 32x32x16 fp8 form: the same 5.9e-3), so a row's LSE, which equals its largest
+# scores, carries an error of about 1e-4 of them: inside the fp8 LSE tolerance (5e-3) up to
+# scores of about 50.  The causal steep ramp reaches 58.7.
+FP8_SCORE_PRECISION = ("fp8 MFMA accumulation keeps ~14 bits relative to the scores: LSE error "
+                       "5.9e-3 at |LSE| = 58.7 (causal ramp10, 520 keys), above 5e-3")
+
+
 @pytest.mark.parametrize("pattern", GROWTH_PATTERNS)
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_running_max_growth(causal, pattern):
-    """As above for e4m3.  The fp8 matrix instruction's dot product keeps about 13 bits
-    relative to the score's magnitude (a causal row that sees one key has LSE = its scaled
-    score; at LSE = 55 its error is 6e-3), so the steep ramp runs over 256 keys, which keeps
-    |LSE| below about 30, where the fp8 LSE tolerance holds."""
-    s = 256 if pattern == "ramp10" else 520
+def test_fp8_running_max_growth(causal, pattern, request):
+    """As above for e4m3, over 520 keys."""
+    if causal and pattern == "ramp10":
+        request.applymarker(pytest.mark.xfail(strict=True, reason=FP8_SCORE_PRECISION))
+    s = 520
     w = fa_inputs.make(1, 4, 2, s, s, 128, causal=causal, seed=90 + GROWTH_PATTERNS.index(pattern),
                        dtype="e4m3", key_offsets=key_offset_pattern(pattern, s),
                        name=f"fp8_growth_{pattern}_s{s}_c{int(causal)}")
+    full_check(w)
+
+
+def test_fp8_large_q_magnitude():
+    """e4m3 counterpart of test_large_q_magnitude: Q x 50 (the q descale grows 50-fold), rows
+    dominated by one key."""
+    w = fa_inputs.make(1, 4, 2, 256, 256, 128, causal=True, seed=61, q_mult=50.0, dtype="e4m3",
+                       name="fp8_q_x50")
+    full_check(w)
+
+
+def test_fp8_moderately_peaked_rows():
+    """e4m3 with Q x 20: rows whose weight is spread over a few keys, where the rounding of P to
+    e4m3 (3 mantissa bits) for the P V product matters most."""
+    w = fa_inputs.make(1, 4, 2, 512, 512, 128, causal=True, seed=62, q_mult=20.0, dtype="e4m3",
+                       name="fp8_q_x20")
     full_check(w)
 
 
@@ -320,9 +362,7 @@ def test_no_writes_outside_outputs(schedule):
 # ------------------------------------------------------------------- fp8 e4m3
 
 def test_fp8_causal_16384_sampled():
-    w = fa_inputs.workload("fp8_causal_b1_h32_s16384_d128")
-    o, lse = sampled_check(w, n_random=32)
-    assert np.isfinite(lse).all() and np.isfinite(o).all()
+    sampled_check(fa_inputs.workload("fp8_causal_b1_h32_s16384_d128"))
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -360,8 +400,11 @@ def kvcache_check(case, name):
     lens = torch.from_numpy(case.cache_seqlens).cuda()
     ds = None if case.descales is None else torch.from_numpy(case.descales).cuda()
     say(f"[gpu] fa_fwd_kvcache {name}")
-    o, lse = fa.forward_kvcache(q, kc, vc, lens, kn, vn, causal=case.causal,
-                                softmax_scale=case.softmax_scale, descales=ds)
+    b, sq, hq, d = case.q.shape
+    o = torch.full((b * sq, hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((hq, b * sq), float("nan"), dtype=torch.float32, device="cuda")
+    fa.forward_kvcache(q, kc, vc, lens, kn, vn, causal=case.causal,
+                       softmax_scale=case.softmax_scale, descales=ds, out=o, lse=lse)
     torch.cuda.synchronize()
     dt = oracle.BF16 if case.dtype == "bf16" else oracle.E4M3
     ro, rl, rk, rv = oracle.attention_kvcache(case.q, case.k_cache, case.v_cache, case.k_new,
@@ -526,8 +569,9 @@ def test_longest_supported_key_range(sq, causal, schedule):
     q = w.q.to("cuda")
     k, v = _repeat_keys(w, reps)
     say(f"[gpu] fa_fwd {w.name}: hq=2 hkv=1 sq={sq} sk={period * reps} d=128 causal={causal}")
-    o, lse = fa.forward(q, k, v, causal=causal, softmax_scale=w.softmax_scale,
-                        max_seqlen_q=sq, max_seqlen_k=period * reps, batch=1)
+    o, lse = nan_outputs(w)
+    fa.forward(q, k, v, causal=causal, softmax_scale=w.softmax_scale, max_seqlen_q=sq,
+               max_seqlen_k=period * reps, batch=1, out=o, lse=lse)
     torch.cuda.synchronize()
     del k, v
     compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro,
@@ -547,8 +591,9 @@ def test_fp8_longest_supported_key_range():
     k, v = _repeat_keys(w, reps)
     ds = torch.from_numpy(w.descales).to("cuda")
     say(f"[gpu] fa_fwd {w.name}: hq=2 hkv=1 sq=64 sk={period * reps} d=128 fp8")
-    o, lse = fa.forward(q, k, v, causal=False, softmax_scale=w.softmax_scale,
-                        max_seqlen_q=64, max_seqlen_k=period * reps, descales=ds, batch=1)
+    o, lse = nan_outputs(w)
+    fa.forward(q, k, v, causal=False, softmax_scale=w.softmax_scale, max_seqlen_q=64,
+               max_seqlen_k=period * reps, descales=ds, batch=1, out=o, lse=lse)
     torch.cuda.synchronize()
     del k, v
     compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro,
