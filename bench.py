@@ -319,9 +319,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported by this "
-              "single-GPU build (the kernel's multi-GPU sharding is a design note, not code).",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported; the "
+              "library runs the forward on one GPU and has no multi-GPU path.", file=sys.stderr)
         return 2
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
