@@ -616,8 +616,8 @@ void fa_fwd_bf16_kernel(Params p) {
 // before their first use, into the buffers whose last readers finished in
 // slot 2k-1; the prologue loads step 0's share (K_{N-1}, K_{N-2}, V_{N-1}).
 // XQ > 0 puts every XQ-th exponential on the FMA polynomial (exp2 offload).
-#ifndef PP_AHEAD
-#define PP_AHEAD 20
+#ifndef PP_LEAD
+#define PP_LEAD 4
 #endif
 template <int D, bool CAUSAL, int XQ>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -851,10 +851,19 @@ void fa_fwd_bf16_pp_kernel(Params p) {
     }
     if (DO_QK && DO_PV) {
       // Only this wave of the SIMD issues MFMAs during the slot, so nothing
-      // else hides LDS latency: keep PP_AHEAD operand reads in flight.
-      sched_group(kSchedDsRead, PP_AHEAD);
+      // else hides LDS latency.  The slot reads 1.5 operands per MFMA (a K
+      // row block for QK^T, two transposed V reads for P V): PP_LEAD reads go
+      // first, then each pair of MFMAs is followed by three reads, so the
+      // reads stay PP_LEAD ahead to the end of the slot.  (A lead that is
+      // large up front and shrinks by half a read per MFMA stalls at both
+      // ends: the first MFMA waits for all but 15 of the reads issued before
+      // it -- the LDS counter's limit -- and the last ones for reads just
+      // issued; measured 0.6-1.4 % slower.)
+      sched_group(kSchedDsRead, PP_LEAD);
 #pragma unroll
-      for (int i = 0; i < 2 * STEPS; ++i) {
+      for (int i = 0; i < (3 * STEPS - PP_LEAD) / 3; ++i) {
+        sched_group(kSchedMfma, 1);
+        sched_group(kSchedDsRead, 2);
         sched_group(kSchedMfma, 1);
         sched_group(kSchedDsRead, 1);
       }
