@@ -107,8 +107,9 @@ def fa_version() -> int:
 
 def fa_set_schedule(schedule: int) -> None:
     """Tuning override of the planner: 0 automatic; 1 one query tile per wave; 2 two query tiles
-    per wave (bf16); 3 the 8-wave ping-pong (bf16, even heads_q / heads_kv); 4 decode (bf16,
-    heads_q / heads_kv * seqlen_q <= 32)."""
+    per wave (bf16); 3 the 8-wave ping-pong (bf16, even heads_q / heads_kv, or odd for fixed
+    lengths); 4 decode (bf16, heads_q / heads_kv * seqlen_q <= 32); 5 the ping-pong's items
+    walked by resident workgroups (persistent launch, where 3 applies)."""
     rc = _lib.fa_set_schedule(int(schedule))
     if rc != 0:
         raise FaError(rc, "fa_set_schedule")

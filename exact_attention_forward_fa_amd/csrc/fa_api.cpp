@@ -67,7 +67,7 @@ int fa_check_cu_seqlens(const int* cu, int batch, int seqlen_q, int seqlen_k, in
 }
 
 int fa_set_schedule(int schedule) {
-  if (schedule < 0 || schedule > 4) return FA_ERR_INVALID;
+  if (schedule < 0 || schedule > 5) return FA_ERR_INVALID;
   g_schedule.store(schedule, std::memory_order_relaxed);
   return FA_OK;
 }
@@ -130,6 +130,10 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   //    KV head -- or, for an odd heads_q / heads_kv (1: MHA), two adjacent
   //    128-row tiles of one head --,
   //    alternating GEMM and softmax slots (ping-pong), 256 registers per lane;
+  //  * schedule 5 (forced only, where 3 applies): the items of schedule 3
+  //    walked by resident workgroups (one per CU), each taking its XCD's
+  //    items in zig-zag windows and prefetching the next item's query rows
+  //    into an LDS stage before the current item's epilogue;
   //  * schedule 4 (bf16, heads_q / heads_kv * seqlen_q <= 32): decode -- all
   //    query rows of one KV head's group in the 32 columns of one tile, one
   //    workgroup per (sequence, KV head) whose 4 waves split the key range in
@@ -174,7 +178,13 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
                          L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;
   const int forced = g_schedule.load(std::memory_order_relaxed);
   int sched = forced ? forced : (decode_ok ? 4 : pp_auto ? 3 : 1);
-  if ((sched == 2 && !wide_ok) || (sched == 3 && !pp_ok) || (sched == 4 && !decode_ok)) sched = 1;
+  // schedule 5: the ping-pong items walked by resident workgroups, with a Q
+  // stage for the next item's rows beside the K/V stages
+  const int64_t q_stage = 2LL * fa::kWaves * 32 * head_dim * 2;
+  const bool persist_ok = pp_ok && lds + q_stage <= L.lds_bytes_per_block && L.num_cus >= fa::kXcds;
+  if ((sched == 2 && !wide_ok) || (sched == 3 && !pp_ok) || (sched == 4 && !decode_ok) ||
+      (sched == 5 && !persist_ok))
+    sched = 1;
   if (sched == 4) {
     out->tile_m = 32;  // (query head, row) columns of one tile
     out->tile_n = 32;
@@ -192,11 +202,12 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
     return FA_OK;
   }
   const int qt = sched == 2 ? 2 : 1;
-  const int waves = sched == 3 ? 2 * fa::kWaves : fa::kWaves;
-  // schedule 3 with an odd heads_q / heads_kv: two adjacent 128-row tiles of
-  // one head per workgroup instead of two heads
-  const bool mpair = sched == 3 && group % 2 == 1;
-  const int heads_per_wg = sched == 3 && !mpair ? 2 : 1;
+  const bool pp = sched == 3 || sched == 5;
+  const int waves = pp ? 2 * fa::kWaves : fa::kWaves;
+  // schedules 3 and 5 with an odd heads_q / heads_kv: two adjacent 128-row
+  // tiles of one head per workgroup instead of two heads
+  const bool mpair = pp && group % 2 == 1;
+  const int heads_per_wg = pp && !mpair ? 2 : 1;
   const int vgprs = 256 * qt;
   const int by_lds = (int)(L.lds_bytes_per_cu / lds);
   const int by_regs = (L.regs_per_simd_lane / vgprs) * L.simds_per_cu / waves;
@@ -204,8 +215,10 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   out->tile_n = fa::kTileN;
   out->waves = waves;
   out->kv_stages = fa::kStages;
-  out->lds_bytes = lds;
-  out->wg_per_cu = by_lds < by_regs ? by_lds : by_regs;
+  out->lds_bytes = sched == 5 ? lds + q_stage : lds;
+  const int by_lds_s = (int)(L.lds_bytes_per_cu / out->lds_bytes);
+  out->wg_per_cu = by_lds_s < by_regs ? by_lds_s : by_regs;
+  (void)by_lds;
   out->vgprs_per_lane = vgprs;
   out->query_tiles = qt;
   out->heads_per_workgroup = heads_per_wg;
@@ -215,6 +228,10 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   // kv-head) pair, the pairs dealt round-robin to the XCDs (the last round padded)
   out->num_workgroups = out->m_tiles == 0 ? 0
                         : rounds * fa::kXcds * out->m_tiles * (int64_t)(group / heads_per_wg);
+  if (sched == 5) {  // resident workgroups: one per CU, a whole number per XCD, at most one per item
+    const int64_t resident = (int64_t)(L.num_cus / fa::kXcds) * fa::kXcds;
+    if (out->num_workgroups > resident) out->num_workgroups = resident;
+  }
   out->kernel_variant = (head_dim == 128 ? 0 : 2) + (causal ? 1 : 0) + (dtype == FA_DTYPE_E4M3 ? 4 : 0);
   if (out->wg_per_cu <= 0) return FA_ERR_UNSUPPORTED;
   return FA_OK;
@@ -278,7 +295,12 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   L.fp8 = dtype == FA_DTYPE_E4M3;
   L.num_workgroups = plan.num_workgroups;
   L.query_tiles = qt;
-  L.pingpong = plan.schedule == 3;
+  L.pingpong = plan.schedule == 3 || plan.schedule == 5;
+  L.persist = plan.schedule == 5;
+  // the items of the one-item kernel's grid, walked by the resident workgroups
+  L.num_items = L.persist ? ((int64_t)batch * heads_kv + fa::kXcds - 1) / fa::kXcds * fa::kXcds *
+                                plan.m_tiles * ((heads_q / heads_kv) / plan.heads_per_workgroup)
+                          : plan.num_workgroups;
   L.decode = plan.schedule == 4;
   L.exp2_offload = L.pingpong ? g_exp2_offload.load(std::memory_order_relaxed) : 0;
   return fa::launch(L, stream);

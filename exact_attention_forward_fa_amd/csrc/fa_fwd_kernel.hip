@@ -630,9 +630,16 @@ void fa_fwd_bf16_kernel(Params p) {
 #ifndef PP_LEAD
 #define PP_LEAD 4
 #endif
-template <int D, bool CAUSAL, int XQ>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_fwd_bf16_pp_kernel(Params p) {
+// One work item of the ping-pong schedule, for the kernel that gives each
+// workgroup one item (PERSIST false) and for the persistent kernel below.
+// smem: 4 * BUF bytes of K/V stages, and with PERSIST a Q stage of 32 rows per
+// wave after them.  wid_in: the item; next_wid (PERSIST): the item this
+// workgroup takes next, whose query rows are prefetched into the Q stage
+// during this one (-1: none); q_in_lds: this item's rows were prefetched so.
+// Returns whether it prefetched.
+template <int D, bool CAUSAL, int XQ, bool PERSIST>
+__device__ __forceinline__ bool pp_item(const Params& p, char* const smem, const int wid_in,
+                                        const int next_wid, const bool q_in_lds) {
   constexpr int TM = kTileM, TN = kTileN;
   constexpr int RB = D * 2;                  // bytes per K/V row in LDS
   constexpr int BUF = TN * RB;               // bytes per K or V block buffer
@@ -642,11 +649,16 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   constexpr int KC = D / 16;                 // k-chunks of the QK^T product
   constexpr int DT = D / 32;                 // 32-wide output tiles of O^T
   static_assert(NI >= 1, "each wave issues at least one load per block");
-  __shared__ __attribute__((aligned(1024))) char smem[4 * BUF];
   char* const kbuf0 = smem;
   char* const vbuf0 = smem + 2 * BUF;
 
-  const int tid = threadIdx.x;
+  // Persistent: the item id is wave-uniform by construction and said so, and
+  // the thread index passes an empty asm per item, so that nothing derived
+  // from it is hoisted out of the item loop (where it would hold registers
+  // through every step of every item).
+  const int wid = PERSIST ? __builtin_amdgcn_readfirstlane(wid_in) : wid_in;
+  int tid = threadIdx.x;
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
   const int wave = tid >> 6;
   const int grp = wave >> 2;  // 0: group A, 1: group B
   // 32-row slice of the tile; group B takes the slices in reverse order, so
@@ -665,24 +677,43 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   // the same K/V blocks, those of the upper tile, whose extra causal blocks
   // are fully masked for the lower one.
   const bool mpair = p.group & 1;
-  const int hpairs = mpair ? p.group : p.group >> 1;  // slots per (tile, KV head)
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int per_pair = p.m_tiles * hpairs;
-  const int kk = slot / per_pair;
-  const int within = slot - kk * per_pair;
-  const int pair = xcd + kXcds * kk;
-  if (pair >= p.batch * p.hkv) return;  // padding of the last round
-  const int b = pair / p.hkv;
-  const int mrev = within / hpairs;
-  const int g = pair - b * p.hkv;
-  const int head = mpair ? g * p.group + (within - mrev * hpairs)
-                         : g * p.group + 2 * (within - mrev * hpairs) + grp;
-  const int mblk = CAUSAL ? (p.m_tiles - 1 - mrev) : mrev;
-  const SeqInfo si = seq_info(p, b);
-  const int m0_wg = mpair ? 2 * mblk * TM : mblk * TM;  // the workgroup's first row
-  if (m0_wg >= si.sq) return;  // uniform over the workgroup, before any barrier
-  const int m0 = mpair ? m0_wg + grp * TM : m0_wg;     // this group's first row
+  struct Item {
+    int g, head, m0_wg, m0;  // KV head, this group's query head, first rows
+    SeqInfo si;
+  };
+  // false for the padding of the last round and for a tile past its
+  // sequence's end (uniform over the workgroup, decided before any barrier)
+  auto decode = [&](const int id, Item& it) __attribute__((always_inline)) {
+    const int hpairs = mpair ? p.group : p.group >> 1;  // slots per (tile, KV head)
+    const int xcd = (unsigned)id % kXcds;
+    const int slot = (unsigned)id / kXcds;
+    const int per_pair = p.m_tiles * hpairs;
+    const int kk = slot / per_pair;
+    const int within = slot - kk * per_pair;
+    const int pair = xcd + kXcds * kk;
+    if (pair >= p.batch * p.hkv) return false;
+    const int b = pair / p.hkv;
+    const int mrev = within / hpairs;
+    it.g = pair - b * p.hkv;
+    it.head = mpair ? it.g * p.group + (within - mrev * hpairs)
+                    : it.g * p.group + 2 * (within - mrev * hpairs) + grp;
+    const int mblk = CAUSAL ? (p.m_tiles - 1 - mrev) : mrev;
+    it.si = seq_info(p, b);
+    if constexpr (PERSIST) {
+      it.si.q0 = __builtin_amdgcn_readfirstlane(it.si.q0);
+      it.si.sq = __builtin_amdgcn_readfirstlane(it.si.sq);
+      it.si.k0 = __builtin_amdgcn_readfirstlane(it.si.k0);
+      it.si.sk = __builtin_amdgcn_readfirstlane(it.si.sk);
+      it.si.total_q = __builtin_amdgcn_readfirstlane(it.si.total_q);
+    }
+    it.m0_wg = mpair ? 2 * mblk * TM : mblk * TM;  // the workgroup's first row
+    it.m0 = mpair ? it.m0_wg + grp * TM : it.m0_wg;  // this group's first row
+    return it.m0_wg < it.si.sq;
+  };
+  Item cur;
+  if (!decode(wid, cur)) return false;
+  const int g = cur.g, head = cur.head, m0_wg = cur.m0_wg, m0 = cur.m0;
+  const SeqInfo si = cur.si;
   const int m0_top = mpair ? m0_wg + TM : m0_wg;       // the upper group's first row
   const int qi = m0 + wv * 32 + r32;
   const bool qvalid = qi < si.sq;
@@ -708,11 +739,11 @@ void fa_fwd_bf16_pp_kernel(Params p) {
       for (int e = hf * 4; e < D; e += 8) *(u32x2*)(O + orow() + e) = u32x2{0u, 0u};
       if (hf == 0) p.lse[lse_idx()] = -INFINITY;
     }
-    return;
+    return false;
   }
 
   bf16x8 qf[KC];
-  {
+  if (!PERSIST || !q_in_lds) {
     const __bf16* qp = Q + orow() + 8 * hf;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -751,6 +782,44 @@ void fa_fwd_bf16_pp_kernel(Params p) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) ka[kc] = r32 * RB + (((2 * kc + hf) ^ x) * 16);
   }
+  // Persistent: this wave's Q stage (its 32 query rows of the next item), 16-byte
+  // chunk c of row r at position c ^ swz_k(r) -- the K layout, so the K operand
+  // offsets address the B operand fragments
+  char* const qwave = smem + 4 * BUF + __builtin_amdgcn_readfirstlane(wave * 32 * RB);
+  if constexpr (PERSIST) {
+    if (q_in_lds) {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qf[kc] = *(const bf16x8*)(qwave + ka[kc]);
+    }
+  }
+  // The next item's rows are loaded into the Q stage in step kq, after that
+  // step's K/V loads; the barrier of step kq + 1 then waits for all but
+  // these NQ loads, and the epilogue for them before its stores.
+  constexpr int NQ = 32 * CPR / 64;  // 16-byte loads per lane
+  const int kq = N > 3 ? N - 2 : 1;
+  bool pf_done = false;
+  auto prefetch_q = [&]() __attribute__((always_inline)) {
+    if constexpr (PERSIST) {
+      Item nx;
+      const int nwid = __builtin_amdgcn_readfirstlane(next_wid);
+      if (nwid < 0 || !decode(nwid, nx)) return;
+      pf_done = true;
+      const int r0 = nx.m0 + wv * 32;
+      const int rows = min(max(nx.si.sq - r0, 0), 32);  // rows past the end arrive as zeros
+      const int rstride = p.hq * D * 2;
+      const char* base = (const char*)p.q + ((int64_t)(nx.si.q0 + r0) * p.hq + nx.head) * D * 2;
+      __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rows * rstride, kRsrcWord3);
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int P = u * 64 + lane;
+        const int row = P / CPR, pos = P % CPR;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void*)(qwave + u * 1024), 16,
+            (unsigned)(row * rstride + ((pos ^ swz_k<D>(row)) * 16)), 0, 0, 0);
+      }
+    }
+  };
   int va[DT];
   {
     const int tr_row = (lane & 15) >> 2;
@@ -893,11 +962,19 @@ void fa_fwd_bf16_pp_kernel(Params p) {
     // for the other waves to read them.  The wait is written out: the
     // barrier's fence does not oblige the compiler to wait for loads, and in
     // some code shapes it does not.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (PERSIST && pf_done && k == kq + 1) {
+      if constexpr (NQ == 8)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
     if (k >= 1) {  // step 0's loads are part of the prologue
       if (N - 2 - k >= 0) stage(kseq, koff, kdst, N - 2 - k);
       if (N - 1 - k >= 0) stage(vseq, voff, vdst, N - 1 - k);
+      if (PERSIST && k == kq) prefetch_q();
     }
     // The two phases follow each other without a barrier (one between them
     // would publish nothing): the step's full barrier starts the groups in
@@ -994,12 +1071,49 @@ void fa_fwd_bf16_pp_kernel(Params p) {
   }
 
   // ---- epilogue
+  // the next item's query rows are in this wave's Q stage before the stores
+  // (later loads would otherwise wait behind them)
+  if (PERSIST && pf_done) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   pin_accumulators(oacc);
   const float l_tot = halfwave_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   store_o_rows<DT>(oacc, inv, O + orow(), hf, qvalid);
   if (qvalid && hf == 0)
     p.lse[lse_idx()] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+  return pf_done;
+}
+
+template <int D, bool CAUSAL, int XQ>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_bf16_pp_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileN * D * 2];
+  pp_item<D, CAUSAL, XQ, false>(p, smem, blockIdx.x, -1, false);
+}
+
+// Persistent ping-pong (schedule 5, forced only): one resident workgroup per
+// CU walking the items of its XCD (item = kXcds * slot + xcd, the order of the
+// one-item kernel: heaviest tiles first, neighbouring slots on one KV head).
+// The gridDim.x / kXcds workgroups of an XCD take its slots in windows of
+// twice their number, zig-zag within each window (workgroup w: slots w and
+// 2G - 1 - w), which balances the causal tiles' work while all of them stay
+// on neighbouring slots, and each prefetches the query rows of its next item
+// before the epilogue of the current one ([FWD-PASS] producer loop: the next
+// work tile is fetched before the epilogue).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_bf16_pp_persist_kernel(Params p, int num_items) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileN * D * 2 + 8 * 32 * D * 2];
+  const int G = gridDim.x / kXcds, w = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
+  const int slots = num_items / kXcds;
+  auto slot_of = [&](const int r) { return 2 * G * (r >> 1) + ((r & 1) ? 2 * G - 1 - w : w); };
+  bool q_in_lds = false;
+  for (int r = 0; 2 * G * (r >> 1) < slots; ++r) {
+    const int slot = slot_of(r), nslot = slot_of(r + 1);
+    if (r > 0) __syncthreads();  // the previous item's readers are done with the stages
+    q_in_lds = slot < slots && pp_item<D, CAUSAL, 0, true>(p, smem, slot * kXcds + x,
+                                                            nslot < slots ? nslot * kXcds + x : -1,
+                                                            q_in_lds);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1605,6 +1719,11 @@ void launch_fp8(const Launch& L, hipStream_t stream) {
 template <int D, bool CAUSAL>
 void launch_bf16_pp(const Launch& L, hipStream_t stream) {
   const dim3 grid((unsigned)L.num_workgroups), block(512);
+  if (L.persist) {
+    hipLaunchKernelGGL((fa_fwd_bf16_pp_persist_kernel<D, CAUSAL>), grid, block, 0, stream, L.p,
+                       (int)L.num_items);
+    return;
+  }
   if (L.exp2_offload == 4)
     hipLaunchKernelGGL((fa_fwd_bf16_pp_kernel<D, CAUSAL, 4>), grid, block, 0, stream, L.p);
   else if (L.exp2_offload == 8)

@@ -50,6 +50,8 @@ struct Launch {
   int pingpong;     // 1: the 8-wave ping-pong kernel (bf16, two query heads per workgroup)
   int decode;       // 1: the decode kernel (bf16, a KV head's query rows in one tile)
   int exp2_offload; // ping-pong only: 0, or every 4th / 8th exponential on the FMA polynomial
+  int persist;      // ping-pong only: 1 for the persistent kernel (num_items items)
+  int64_t num_items;
   int64_t num_workgroups;
 };
 

@@ -215,7 +215,7 @@ typedef struct fa_plan {
   int kernel_variant;    /* index of the compiled kernel                      */
   int query_tiles;       /* 32-row query tiles per wave                       */
   int heads_per_workgroup; /* query heads sharing one workgroup's K/V staging  */
-  int schedule;          /* 1, 2, 3 or 4 (see fa_fwd_plan)                    */
+  int schedule;          /* 1 to 5 (see fa_fwd_plan)                          */
 } fa_plan_t;
 
 /*
@@ -243,7 +243,18 @@ typedef struct fa_plan {
  *   4  bf16, heads_q / heads_kv * seqlen_q <= 32 (decode): the (query head,
  *      row) pairs of one KV head in the 32 columns of one tile, one workgroup
  *      per (sequence, KV head) whose 4 waves split the key range and merge
- *      their partial softmax states at the end.
+ *      their partial softmax states at the end;
+ *   5  forced only, where 3 applies: schedule 3's work items walked by
+ *      resident workgroups (a persistent launch: num_workgroups = the CUs, a
+ *      whole number per XCD, at most the number of items), each taking its
+ *      XCD's items in the order of schedule 3's grid, zig-zag in windows of
+ *      twice the workgroups per XCD, and loading the next item's query rows
+ *      into an LDS stage (lds_bytes includes it) during the current item --
+ *      the persistent tile scheduler of "FlashAttention core algorithm:
+ *      forward pass" (producer loop: the next work tile fetched before the
+ *      epilogue).  It computes what schedule 3 computes; it measures slower
+ *      on gfx950, where the hardware dispatcher already hands out schedule
+ *      3's workgroups heaviest first as CUs free up.
  * The plan uses 4 where it applies, else 3 where it applies and its grid has
  * at least one workgroup per CU (`dev->num_cus`; smaller grids finish first
  * on schedule 1's finer tiles), from 2048 query rows unless its grid is a
@@ -258,7 +269,7 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
 /*
  * fa_set_schedule -- tuning override of the planner's schedule choice (for
  * benchmarking and for tests that run every schedule on the same shapes).
- * 0 restores the automatic choice; 1, 2, 3 or 4 forces that schedule in every
+ * 0 restores the automatic choice; 1, 2, 3, 4 or 5 forces that schedule in every
  * later fa_fwd / fa_fwd_kvcache / fa_fwd_plan call of the process wherever it
  * applies (schedule 1 elsewhere).  All schedules compute the same function to
  * within rounding, but not bit for bit: the reference maximum that the

@@ -280,7 +280,26 @@ def test_schedule_override():
         assert fa.fa_fwd_plan(*args).schedule == 1
         assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 32, 8, 1, 8192, False, 128, 128,
                               True).schedule == 4
-        for bad in (-1, 5):
+        # schedule 5: schedule 3's items on resident workgroups -- one per CU (a whole
+        # number per XCD), at most one per item; the LDS holds a Q stage of 32 rows per wave
+        fa.fa_set_schedule(5)
+        p = fa.fa_fwd_plan(*args)
+        assert (p.schedule, p.waves, p.tile_m, p.heads_per_workgroup, p.m_tiles) == (5, 8, 128, 2, 64)
+        assert (p.num_workgroups, p.wg_per_cu) == (256, 1)
+        assert p.lds_bytes == 4 * 64 * 128 * 2 + 8 * 32 * 128 * 2
+        small = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 4, 2, 256, 256, False, 64, 64, True)
+        assert (small.schedule, small.num_workgroups) == (5, 8 * 2 * 1)  # one padded round
+        # where schedule 3 does not apply (fp8, odd groups in packed batches): 1
+        assert fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 2, 32, 8, 8192, 8192, False, 128, 128,
+                              True).schedule == 1
+        assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 3, 1, 300, 300, True, 64, 64,
+                              False).schedule == 1
+        # a device with fewer CUs than XCDs cannot hold a whole number per XCD
+        lim = fa.fa_gfx950_limits()
+        lim.num_cus = 4
+        p4 = fa.fa_fwd_plan(*args, dev=lim)
+        assert p4.schedule == 1
+        for bad in (-1, 6):
             with pytest.raises(fa.FaError) as e:
                 fa.fa_set_schedule(bad)
             assert e.value.code == fa.FA_ERR_INVALID

@@ -12,11 +12,13 @@ from parity import (check_written, compare, gather_rows, gpu_run, nan_outputs, o
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=[1, 2, 3, 4], ids=["sched1", "sched2", "sched3", "sched4"])
+@pytest.fixture(params=[1, 2, 3, 4, 5], ids=["sched1", "sched2", "sched3", "sched4", "sched5"])
 def schedule(request):
     """Force each bf16 schedule (1: one query tile per wave; 2: two; 3: 8-wave ping-pong,
     where heads_q / heads_kv is even (two heads per workgroup) or 1 (two adjacent query tiles
-    of one head); 4: decode, where heads_q / heads_kv * seqlen_q <= 32; else 1) for the test."""
+    of one head); 4: decode, where heads_q / heads_kv * seqlen_q <= 32; 5: schedule 3's items
+    on resident workgroups (persistent launch, next item's query rows prefetched), where 3
+    applies; else 1) for the test."""
     import exact_attention_forward_fa_amd as fa
 
     fa.fa_set_schedule(request.param)

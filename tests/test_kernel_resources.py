@@ -66,8 +66,9 @@ def _plan(schedule, d, dtype):
 
 def _classify(name):
     """(schedule, head_dim, dtype) of a mangled kernel name, or None for non-attention kernels."""
-    m = re.search(r"(fa_fwd_bf16_kernel|fa_fwd_bf16_pp_kernel|fa_fwd_bf16_decode_kernel|"
-                  r"fa_fwd_fp8_kernel|fa_fwd_fp8_pp_kernel)ILi(\d+)ELb([01])E(?:Li(\d+)E)?", name)
+    m = re.search(r"(fa_fwd_bf16_kernel|fa_fwd_bf16_pp_kernel|fa_fwd_bf16_pp_persist_kernel|"
+                  r"fa_fwd_bf16_decode_kernel|fa_fwd_fp8_kernel)ILi(\d+)ELb([01])E(?:Li(\d+)E)?",
+                  name)
     if not m:
         return None
     kind, d = m.group(1), int(m.group(2))
@@ -76,10 +77,10 @@ def _classify(name):
         return (1 if extra == 1 else 2), d, fa.FA_DTYPE_BF16
     if kind == "fa_fwd_bf16_pp_kernel":
         return 3, d, fa.FA_DTYPE_BF16
+    if kind == "fa_fwd_bf16_pp_persist_kernel":
+        return 5, d, fa.FA_DTYPE_BF16
     if kind == "fa_fwd_bf16_decode_kernel":
         return 4, d, fa.FA_DTYPE_BF16
-    if kind == "fa_fwd_fp8_pp_kernel":
-        return 3, d, fa.FA_DTYPE_E4M3
     return 1, d, fa.FA_DTYPE_E4M3
 
 
@@ -88,17 +89,24 @@ def _classify(name):
 # v_readlane in the prologue, at the loop transition and in the epilogue; no memory, nothing in
 # the key-block loop).  The non-causal ping-pong kernels do the same since their steady loop
 # runs in pairs of steps with constant buffer offsets (one or two v_readlane per step, measured
-# faster than the unpaired loop without them).  The counts are pinned at what the current
-# compiler does, so that an increase fails; every other kernel must have none.  Key: (kernel,
-# head_dim, causal, queries per wave for the 4-wave kernels / exp2 offload for ping-pong).
+# faster than the unpaired loop without them).  The persistent ping-pong kernel (schedule 5, an
+# opt-in) carries its item loop's state as well and reloads 20-30 such values per step.  The
+# counts are pinned at what the current compiler does, so that an increase fails; every other
+# kernel must have none.  Key: (kernel, head_dim, causal, queries per wave for the 4-wave
+# kernels / exp2 offload for the ping-pong kernel / None for the persistent one).
 SGPR_LANE_SPILLS = {("fa_fwd_bf16_kernel", 128, 0, 1): 29, ("fa_fwd_bf16_kernel", 64, 0, 1): 21,
                     ("fa_fwd_bf16_kernel", 128, 0, 2): 36, ("fa_fwd_bf16_kernel", 64, 0, 2): 28,
-                    ("fa_fwd_bf16_pp_kernel", 128, 0, 0): 18, ("fa_fwd_bf16_pp_kernel", 128, 0, 4): 19,
-                    ("fa_fwd_bf16_pp_kernel", 128, 0, 8): 19, ("fa_fwd_bf16_pp_kernel", 64, 0, 0): 14,
-                    ("fa_fwd_bf16_pp_kernel", 64, 0, 4): 15, ("fa_fwd_bf16_pp_kernel", 64, 0, 8): 15}
+                    ("fa_fwd_bf16_pp_kernel", 128, 0, 0): 22, ("fa_fwd_bf16_pp_kernel", 128, 0, 4): 23,
+                    ("fa_fwd_bf16_pp_kernel", 128, 0, 8): 23, ("fa_fwd_bf16_pp_kernel", 64, 0, 0): 18,
+                    ("fa_fwd_bf16_pp_kernel", 64, 0, 4): 19, ("fa_fwd_bf16_pp_kernel", 64, 0, 8): 19}
+# (head_dim, causal) of the persistent ping-pong kernel
+PERSIST_LANE_SPILLS = {(128, 0): 61, (128, 1): 61, (64, 0): 54, (64, 1): 54}
 
 
 def _sgpr_allowance(name):
+    m = re.search(r"fa_fwd_bf16_pp_persist_kernelILi(\d+)ELb([01])E", name)
+    if m:
+        return PERSIST_LANE_SPILLS.get((int(m.group(1)), int(m.group(2))), 0)
     m = re.search(r"(fa_fwd_bf16_kernel|fa_fwd_bf16_pp_kernel)ILi(\d+)ELb([01])ELi(\d+)E", name)
     if not m:
         return 0
@@ -131,6 +139,6 @@ def test_attention_kernels_match_their_plans(usage):
         seen.add((sched, d, dtype))
     # every schedule of both head dims (bf16) and the fp8 kernels were found
     for d in (64, 128):
-        for s in (1, 2, 3, 4):
+        for s in (1, 2, 3, 4, 5):
             assert (s, d, fa.FA_DTYPE_BF16) in seen, (s, d)
         assert (1, d, fa.FA_DTYPE_E4M3) in seen, d
