@@ -971,11 +971,18 @@ __device__ __forceinline__ bool pp_item(const Params& p, char* const smem, const
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
-    if (k >= 1) {  // step 0's loads are part of the prologue
-      if (N - 2 - k >= 0) stage(kseq, koff, kdst, N - 2 - k);
-      if (N - 1 - k >= 0) stage(vseq, voff, vdst, N - 1 - k);
-      if (PERSIST && k == kq) prefetch_q();
-    }
+    // Group A issues its share of the step's loads at the step start, group B
+    // after its softmax phase, so that B's softmax -- running beside A's
+    // GEMM phase -- starts at once (measured +0.8 % on the bench workload,
+    // +0.6 to +1.5 % elsewhere; A's share after its GEMM phase: -0.6 %)
+    auto loads = [&]() __attribute__((always_inline)) {
+      if (k >= 1) {  // step 0's loads are part of the prologue
+        if (N - 2 - k >= 0) stage(kseq, koff, kdst, N - 2 - k);
+        if (N - 1 - k >= 0) stage(vseq, voff, vdst, N - 1 - k);
+        if (PERSIST && k == kq) prefetch_q();
+      }
+    };
+    if (grp == 0) loads();
     // The two phases follow each other without a barrier (one between them
     // would publish nothing): the step's full barrier starts the groups in
     // opposite phases, a group that finishes its first phase early starts its
@@ -1009,6 +1016,7 @@ __device__ __forceinline__ bool pp_item(const Params& p, char* const smem, const
       if (k < N && !sk_q) softmax(N - 1 - k);
     } else {
       if (k >= 1 && !sk_p) softmax(N - k);
+      loads();
       __builtin_amdgcn_s_setprio(1);
       gemm_sk();
       __builtin_amdgcn_s_setprio(0);

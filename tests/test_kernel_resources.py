@@ -96,11 +96,11 @@ def _classify(name):
 # kernels / exp2 offload for the ping-pong kernel / None for the persistent one).
 SGPR_LANE_SPILLS = {("fa_fwd_bf16_kernel", 128, 0, 1): 29, ("fa_fwd_bf16_kernel", 64, 0, 1): 21,
                     ("fa_fwd_bf16_kernel", 128, 0, 2): 36, ("fa_fwd_bf16_kernel", 64, 0, 2): 28,
-                    ("fa_fwd_bf16_pp_kernel", 128, 0, 0): 22, ("fa_fwd_bf16_pp_kernel", 128, 0, 4): 23,
-                    ("fa_fwd_bf16_pp_kernel", 128, 0, 8): 23, ("fa_fwd_bf16_pp_kernel", 64, 0, 0): 18,
-                    ("fa_fwd_bf16_pp_kernel", 64, 0, 4): 19, ("fa_fwd_bf16_pp_kernel", 64, 0, 8): 19}
+                    ("fa_fwd_bf16_pp_kernel", 128, 0, 0): 20, ("fa_fwd_bf16_pp_kernel", 128, 0, 4): 21,
+                    ("fa_fwd_bf16_pp_kernel", 128, 0, 8): 21, ("fa_fwd_bf16_pp_kernel", 64, 0, 0): 14,
+                    ("fa_fwd_bf16_pp_kernel", 64, 0, 4): 14, ("fa_fwd_bf16_pp_kernel", 64, 0, 8): 14}
 # (head_dim, causal) of the persistent ping-pong kernel
-PERSIST_LANE_SPILLS = {(128, 0): 61, (128, 1): 61, (64, 0): 54, (64, 1): 54}
+PERSIST_LANE_SPILLS = {(128, 0): 61, (128, 1): 69, (64, 0): 54, (64, 1): 58}
 
 
 def _sgpr_allowance(name):
