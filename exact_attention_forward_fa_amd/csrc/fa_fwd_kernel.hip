@@ -1,6 +1,6 @@
 // fa_fwd_kernel.hip -- exact attention forward for gfx950 (MI355X, CDNA4).
 //
-// Four schedules of one computation (the planner in fa_api.cpp picks one):
+// Five schedules of one computation (the planner in fa_api.cpp picks one):
 //  1. fa_fwd_bf16_kernel<.., QG = 1> / fa_fwd_fp8_kernel: 4 waves = 128 query
 //     rows of one (sequence, head), two workgroups per CU;
 //  2. fa_fwd_bf16_kernel<.., QG = 2>: 256 rows, one wave per SIMD;
@@ -8,7 +8,9 @@
 //     with an odd number of query heads per KV head, two adjacent query tiles of one), the
 //     two groups of waves alternating GEMM and softmax phases (ping-pong);
 //  4. fa_fwd_bf16_decode_kernel: a KV head's (query head, row) pairs in one
-//     32-column tile, the 4 waves splitting the key range.
+//     32-column tile, the 4 waves splitting the key range;
+//  5. fa_fwd_bf16_pp_persist_kernel (forced only): schedule 3's items walked
+//     by resident workgroups that prefetch their next item's query rows.
 // The description below is that of schedule 1; the others say how they
 // differ.  One workgroup = 4 wavefronts = 128 query rows of one (sequence,
 // head).  Each wave owns 32 query rows and walks the key blocks (64 keys
