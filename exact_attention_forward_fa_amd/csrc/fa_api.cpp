@@ -145,7 +145,6 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const int64_t lds = fa::lds_bytes(head_dim, dtype == FA_DTYPE_E4M3 ? 1 : 2);
   if (lds > L.lds_bytes_per_block) return FA_ERR_UNSUPPORTED;
   const int64_t pairs = (int64_t)batch * heads_kv;
-  const int64_t rounds = (pairs + fa::kXcds - 1) / fa::kXcds;
   const int group = heads_q / heads_kv;
   const bool bf16 = dtype == FA_DTYPE_BF16;
   const bool wide_ok = bf16 && L.regs_per_simd_lane >= 512;
@@ -225,9 +224,10 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   out->schedule = sched;
   out->m_tiles = (seqlen_q + out->tile_m - 1) / out->tile_m;
   // one slot per (query tile, query head or head pair) of every (sequence,
-  // kv-head) pair, the pairs dealt round-robin to the XCDs (the last round padded)
+  // kv-head) pair: whole rounds of kXcds pairs dealt to the XCDs, the other
+  // pairs' items spread over all of them (fa::prefill_grid)
   out->num_workgroups = out->m_tiles == 0 ? 0
-                        : rounds * fa::kXcds * out->m_tiles * (int64_t)(group / heads_per_wg);
+                        : fa::prefill_grid(pairs, out->m_tiles, group / heads_per_wg).workgroups;
   if (sched == 5) {  // resident workgroups: one per CU, a whole number per XCD, at most one per item
     const int64_t resident = (int64_t)(L.num_cus / fa::kXcds) * fa::kXcds;
     if (out->num_workgroups > resident) out->num_workgroups = resident;
@@ -289,6 +289,14 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   L.p.seqlen_q = seqlen_q;
   L.p.seqlen_k = seqlen_k;
   L.p.m_tiles = plan.m_tiles;
+  if (plan.schedule != 4) {
+    const fa::Grid gr = fa::prefill_grid((int64_t)batch * heads_kv, plan.m_tiles,
+                                         (heads_q / heads_kv) / plan.heads_per_workgroup);
+    L.p.full_pairs = (int)gr.full_pairs;
+    L.p.lin_items = (int)gr.lin_items;
+  } else {
+    L.p.full_pairs = L.p.lin_items = 0;
+  }
   L.p.scale_log2 = softmax_scale * kLog2e;
   L.head_dim = head_dim;
   L.causal = causal;
@@ -298,8 +306,9 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   L.pingpong = plan.schedule == 3 || plan.schedule == 5;
   L.persist = plan.schedule == 5;
   // the items of the one-item kernel's grid, walked by the resident workgroups
-  L.num_items = L.persist ? ((int64_t)batch * heads_kv + fa::kXcds - 1) / fa::kXcds * fa::kXcds *
-                                plan.m_tiles * ((heads_q / heads_kv) / plan.heads_per_workgroup)
+  L.num_items = L.persist ? fa::prefill_grid((int64_t)batch * heads_kv, plan.m_tiles,
+                                             (heads_q / heads_kv) / plan.heads_per_workgroup)
+                                .workgroups
                           : plan.num_workgroups;
   L.decode = plan.schedule == 4;
   L.exp2_offload = L.pingpong ? g_exp2_offload.load(std::memory_order_relaxed) : 0;

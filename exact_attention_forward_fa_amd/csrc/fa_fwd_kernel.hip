@@ -119,6 +119,44 @@ __device__ __forceinline__ SeqInfo seq_info(const Params& p, int b) {
   return s;
 }
 
+// The work item of a prefill workgroup: (sequence, KV head) pair, query tile
+// counted from the heaviest (mrev; the last tile under causal masking), and
+// head slot within the pair (hsub < hslots).  Workgroups are dispatched
+// round-robin over the XCDs (block id mod kXcds), each XCD with its own L2.
+// Whole rounds of kXcds pairs are dealt to the XCDs (pair = xcd + kXcds*k):
+// an XCD works through its pairs one at a time, heaviest query tiles first,
+// all head slots side by side, so the workgroups resident on one XCD share
+// one pair's K/V in its L2.  The pairs left over from whole rounds (all of
+// them when there are fewer than kXcds, e.g. one sequence with a few KV
+// heads) would leave XCDs idle that way; their items come first in the grid
+// instead, heaviest tiles of every such pair first, spread over all XCDs
+// (p.lin_items ids, padded to a multiple of kXcds so that the dealt part
+// keeps block id mod kXcds = XCD).  False for padding.
+struct ItemIdx {
+  int pair, mrev, hsub;
+};
+__device__ __forceinline__ bool item_index(const Params& p, const unsigned id, const int hslots,
+                                           ItemIdx& it) {
+  if ((int)id < p.lin_items) {
+    const int per_tile = (p.batch * p.hkv - p.full_pairs) * hslots;
+    it.mrev = (int)id / per_tile;
+    const int rem = (int)id - it.mrev * per_tile;
+    it.pair = p.full_pairs + rem / hslots;
+    it.hsub = rem - (rem / hslots) * hslots;
+    return it.mrev < p.m_tiles;
+  }
+  const unsigned id2 = id - (unsigned)p.lin_items;
+  const int xcd = id2 % kXcds;
+  const int slot = id2 / kXcds;
+  const int per_pair = p.m_tiles * hslots;
+  const int kk = slot / per_pair;
+  const int within = slot - kk * per_pair;
+  it.pair = xcd + kXcds * kk;
+  it.mrev = within / hslots;
+  it.hsub = within - it.mrev * hslots;
+  return it.pair < p.full_pairs;
+}
+
 // A row max may grow by up to kLazy (in exp2 units) before O and l are
 // rescaled: P then stays <= 2^kLazy = kLazyBound, and O / l is unchanged
 // because both are taken relative to the same stale maximum.
@@ -248,22 +286,12 @@ void fa_fwd_bf16_kernel(Params p) {
   const int r32 = lane & 31;
   const int hf = lane >> 5;
 
-  // ---- work item.  Workgroups are dispatched round-robin over the XCDs
-  // (block id mod kXcds), each XCD with its own L2.  The (sequence, kv-head)
-  // pairs are dealt to the XCDs (pair = xcd + kXcds*k), and an XCD works
-  // through its pairs one at a time, heaviest query tiles first, all query
-  // heads of the group side by side -- so the workgroups resident on one XCD
-  // share one pair's K/V in its L2.
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int per_pair = p.m_tiles * p.group;
-  const int kk = slot / per_pair;
-  const int within = slot - kk * per_pair;
-  const int pair = xcd + kXcds * kk;
-  if (pair >= p.batch * p.hkv) return;  // padding of the last round
+  // ---- work item: one query head per head slot
+  ItemIdx itx;
+  if (!item_index(p, blockIdx.x, p.group, itx)) return;  // padding
+  const int pair = itx.pair, mrev = itx.mrev;
   const int b = pair / p.hkv;
-  const int mrev = within / p.group;
-  const int head = (pair - b * p.hkv) * p.group + (within - mrev * p.group);
+  const int head = (pair - b * p.hkv) * p.group + itx.hsub;
   const int mblk = CAUSAL ? (p.m_tiles - 1 - mrev) : mrev;
   const SeqInfo si = seq_info(p, b);
   const int m0 = mblk * TM;
@@ -687,18 +715,12 @@ __device__ __forceinline__ bool pp_item(const Params& p, char* const smem, const
   // sequence's end (uniform over the workgroup, decided before any barrier)
   auto decode = [&](const int id, Item& it) __attribute__((always_inline)) {
     const int hpairs = mpair ? p.group : p.group >> 1;  // slots per (tile, KV head)
-    const int xcd = (unsigned)id % kXcds;
-    const int slot = (unsigned)id / kXcds;
-    const int per_pair = p.m_tiles * hpairs;
-    const int kk = slot / per_pair;
-    const int within = slot - kk * per_pair;
-    const int pair = xcd + kXcds * kk;
-    if (pair >= p.batch * p.hkv) return false;
+    ItemIdx itx;
+    if (!item_index(p, (unsigned)id, hpairs, itx)) return false;
+    const int pair = itx.pair, mrev = itx.mrev;
     const int b = pair / p.hkv;
-    const int mrev = within / hpairs;
     it.g = pair - b * p.hkv;
-    it.head = mpair ? it.g * p.group + (within - mrev * hpairs)
-                    : it.g * p.group + 2 * (within - mrev * hpairs) + grp;
+    it.head = mpair ? it.g * p.group + itx.hsub : it.g * p.group + 2 * itx.hsub + grp;
     const int mblk = CAUSAL ? (p.m_tiles - 1 - mrev) : mrev;
     it.si = seq_info(p, b);
     if constexpr (PERSIST) {
@@ -1455,17 +1477,12 @@ void fa_fwd_fp8_kernel(Params p) {
   const int r32 = lane & 31;
   const int hf = lane >> 5;
 
-  // ---- work item (XCD-aware, as in the bf16 kernel)
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int per_pair = p.m_tiles * p.group;
-  const int kk = slot / per_pair;
-  const int within = slot - kk * per_pair;
-  const int pair = xcd + kXcds * kk;
-  if (pair >= p.batch * p.hkv) return;
+  // ---- work item (as in the bf16 kernel)
+  ItemIdx itx;
+  if (!item_index(p, blockIdx.x, p.group, itx)) return;  // padding
+  const int pair = itx.pair, mrev = itx.mrev;
   const int b = pair / p.hkv;
-  const int mrev = within / p.group;
-  const int head = (pair - b * p.hkv) * p.group + (within - mrev * p.group);
+  const int head = (pair - b * p.hkv) * p.group + itx.hsub;
   const int mblk = CAUSAL ? (p.m_tiles - 1 - mrev) : mrev;
   const SeqInfo si = seq_info(p, b);
   const int m0 = mblk * TM;

@@ -23,6 +23,19 @@ constexpr int64_t lds_bytes(int d, int elem_bytes) {
   return (int64_t)kStages * 2 * kTileN * d * elem_bytes;
 }
 
+// Grid of a prefill schedule with `slots` workgroups per (query tile, pair):
+// the items of the pairs beyond whole rounds of kXcds first (padded to a
+// multiple of kXcds), then whole rounds dealt to the XCDs.
+struct Grid {
+  int64_t full_pairs, lin_items, workgroups;
+};
+constexpr Grid prefill_grid(int64_t pairs, int64_t m_tiles, int64_t slots) {
+  const int64_t full = pairs / kXcds * kXcds;
+  const int64_t lin = (pairs - full) * m_tiles * slots;
+  const int64_t lin_padded = (lin + kXcds - 1) / kXcds * kXcds;
+  return Grid{full, lin_padded, lin_padded + full * m_tiles * slots};
+}
+
 struct Params {
   const void* q;
   const void* k;
@@ -38,6 +51,10 @@ struct Params {
   int seqlen_new;
   int batch, hq, hkv, group, seqlen_q, seqlen_k;
   int m_tiles;            // query tiles per (sequence, head)
+  // grid layout: the pairs of whole rounds of kXcds (full_pairs of them) are
+  // dealt to the XCDs after the first lin_items ids, which spread the items
+  // of the remaining pairs over all XCDs (a multiple of kXcds)
+  int full_pairs, lin_items;
   float scale_log2;       // softmax_scale * log2(e)
 };
 

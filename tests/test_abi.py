@@ -215,11 +215,16 @@ def test_plan_gfx950():
     p2100 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 2100, 2100, False, 128, 128, False)
     assert (p2100.schedule, p2100.m_tiles, p2100.num_workgroups) == (3, 9, 8 * 8 * 9)
     # fewer ping-pong workgroups than CUs: schedule 1's finer grid (one query tile per wave);
-    # 2 (batch, kv-head) pairs dealt to 8 XCDs: one padded round of 8 pairs x 2 tiles x 1 head
+    # 2 (batch, kv-head) pairs, fewer than the 8 XCDs: their 2 tiles x 1 head each are spread
+    # over all XCDs (4 items, padded to 8) instead of being dealt to 2 of them
     p64 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 2, 2, 256, 256, False, 64, 64, False)
     assert (p64.schedule, p64.tile_m, p64.query_tiles, p64.wg_per_cu, p64.vgprs_per_lane) == \
         (1, 128, 1, 2, 256)
-    assert p64.m_tiles == 2 and p64.num_workgroups == 8 * 2 and p64.lds_bytes < p.lds_bytes
+    assert p64.m_tiles == 2 and p64.num_workgroups == 8 and p64.lds_bytes < p.lds_bytes
+    # 12 pairs: one round of 8 dealt to the XCDs (8 x 8 tiles) after the 4 others' items
+    # spread over all XCDs (4 x 8 tiles = 32, a multiple of 8)
+    p12 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 3, 4, 4, 1024, 1024, False, 128, 128, True)
+    assert (p12.schedule, p12.m_tiles, p12.num_workgroups) == (1, 8, 32 + 8 * 8)
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 2, 512, 512, False, 128, 128, True).schedule == 1
     # causal tile pairs over several rounds below 8192 rows: schedule 1; non-causal: pairs
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 2048, 2048, False, 128, 128, True).schedule == 1
@@ -267,8 +272,8 @@ def test_schedule_override():
         fa.fa_set_schedule(3)
         odd = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 3, 1, 300, 300, False, 64, 64, False)
         assert (odd.schedule, odd.waves, odd.heads_per_workgroup, odd.tile_m) == (3, 8, 1, 256)
-        # 2 tile pairs x 3 heads per kv-head, one padded round of 8 (batch, kv-head) pairs
-        assert (odd.m_tiles, odd.num_workgroups) == (2, 8 * 2 * 3)
+        # one (batch, kv-head) pair: its 2 tile pairs x 3 heads spread over the XCDs, 6 -> 8
+        assert (odd.m_tiles, odd.num_workgroups) == (2, 8)
         # ... but not for packed varlen batches: falls back to 1
         oddv = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 3, 1, 300, 300, True, 64, 64, False)
         assert (oddv.schedule, oddv.waves, oddv.heads_per_workgroup) == (1, 4, 1)
@@ -288,7 +293,7 @@ def test_schedule_override():
         assert (p.num_workgroups, p.wg_per_cu) == (256, 1)
         assert p.lds_bytes == 4 * 64 * 128 * 2 + 8 * 32 * 128 * 2
         small = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 4, 2, 256, 256, False, 64, 64, True)
-        assert (small.schedule, small.num_workgroups) == (5, 8 * 2 * 1)  # one padded round
+        assert (small.schedule, small.num_workgroups) == (5, 8)  # 2 pairs x 2 tiles, padded
         # where schedule 3 does not apply (fp8, odd groups in packed batches): 1
         assert fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 2, 32, 8, 8192, 8192, False, 128, 128,
                               True).schedule == 1

@@ -103,6 +103,17 @@ def test_varlen_causal_sampled():
     sampled_check(w)
 
 
+@pytest.mark.parametrize("shape", [(3, 8, 4, 300, 300, True), (9, 2, 1, 200, 330, False),
+                                   (1, 8, 1, 520, 520, True), (2, 4, 2, 130, 260, True)])
+def test_grid_layouts(shape, schedule):
+    """Pair counts that are not whole rounds of the 8 XCDs: 12 (one dealt round, 4 pairs spread),
+    9 (one round, 1 spread), 1 and 4 (all spread), under every schedule."""
+    b, hq, hkv, sq, sk, causal = shape
+    w = fa_inputs.make(b, hq, hkv, sq, sk, 128, causal=causal, seed=sq + 3 * hq + 7 * b,
+                       name=f"grid_b{b}_hq{hq}_hkv{hkv}_{sq}x{sk}_c{int(causal)}")
+    full_check(w)
+
+
 def test_varlen_equals_per_sequence_calls(schedule):
     """Packed varlen output equals separate fixed-length calls, bit for bit (same tiling)."""
     lens = [(300, 517), (1, 64), (129, 100), (64, 0), (0, 40), (255, 256), (70, 700)]
