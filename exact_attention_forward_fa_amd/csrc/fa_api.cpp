@@ -171,7 +171,14 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   // +3.4 %): its two workgroups per CU overlap each other's tile starts.
   const bool one_round = pp_items <= L.num_cus;
   const bool pairs_ok = group % 2 == 0 || !causal || seqlen_q >= 8192 || one_round;
-  const bool pp_auto = pp_ok && pp_items >= L.num_cus && pairs_ok && (seqlen_q >= 2048 || one_round);
+  // A single causal round over at most kXcds (sequence, KV head) pairs: its
+  // critical path is the heaviest item, which schedule 1 finishes 6-11 %
+  // sooner (one sequence with 1, 4 or 8 KV heads, 1024-8192 rows, head pairs
+  // and tile pairs alike); with 16 or more pairs the ping-pong wins (+9 to
+  // +13 %).
+  const bool few_pairs_round = causal && one_round && pairs <= fa::kXcds;
+  const bool pp_auto = pp_ok && pp_items >= L.num_cus && pairs_ok &&
+                       (seqlen_q >= 2048 || one_round) && !few_pairs_round;
   const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&
                          L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;

@@ -259,7 +259,8 @@ typedef struct fa_plan {
  * at least one workgroup per CU (`dev->num_cus`; smaller grids finish first
  * on schedule 1's finer tiles), from 2048 query rows unless its grid is a
  * single round (one workgroup per CU), with tile pairs under causal masking
- * only from 8192 query rows or for a single round, else 1, unless
+ * only from 8192 query rows or for a single round, and not for a single
+ * causal round over at most 8 (sequence, KV head) pairs; else 1, unless
  * fa_set_schedule forces one.
  */
 int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,

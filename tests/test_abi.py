@@ -252,6 +252,11 @@ def test_plan_gfx950():
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 4, 100, False, 64, 64, False).schedule == 4
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 5, 100, False, 64, 64, False).schedule == 1
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 64, 8, 1, 5, 100, False, 64, 64, False).schedule == 3
+    # a single causal round over at most 8 (sequence, kv-head) pairs: schedule 1; 16 pairs: 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 32, 8, 2048, 2048, False, 128, 128, True).schedule == 1
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 32, 1, 2048, 2048, False, 128, 128, True).schedule == 1
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 16, 8, 2048, 2048, False, 128, 128, True).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 32, 8, 2048, 2048, False, 128, 128, False).schedule == 3
     # fp8 never takes it
     assert fa.fa_fwd_plan(fa.FA_DTYPE_E4M3, 32, 32, 8, 1, 8192, False, 128, 128, True).schedule == 1
 
