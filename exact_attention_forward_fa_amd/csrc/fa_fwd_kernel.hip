@@ -496,7 +496,7 @@ void fa_fwd_bf16_kernel(Params p) {
 #pragma unroll
       for (int q = 0; q < QG; ++q) {
         const float pv = exp2_fast(__builtin_fmaf(sc[q][tt][r], c, -ms[q]));
-        rs[q] += pv;
+        rs[q] = idx == 0 ? pv : rs[q] + pv;  // (0 + p is not folded)
         pb[q][2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
       }
     };
@@ -905,7 +905,7 @@ __device__ __forceinline__ bool pp_item(const Params& p, char* const smem, const
         // XQ > 0: every XQ-th exponential on the FMA polynomial (exp2 offload)
         const float x = __builtin_fmaf(sc[tt][r], c, -ms);
         const float pv = (XQ > 0 && idx % XQ == XQ - 1) ? exp2_poly(x) : exp2_fast(x);
-        rs += pv;
+        rs = idx == 0 ? pv : rs + pv;  // (0 + p is not folded)
         pb[2 * tt + (r >> 3)][r & 7] = (__bf16)pv;
       }
       return rs;
@@ -1341,7 +1341,7 @@ void fa_fwd_bf16_decode_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = exp2_fast(__builtin_fmaf(sc[r], c, -ms));
-        rs += pv;
+        rs = r == 0 ? pv : rs + pv;  // (0 + p is not folded)
         pb[r >> 3][r & 7] = (__bf16)pv;
       }
       l_run += rs;
