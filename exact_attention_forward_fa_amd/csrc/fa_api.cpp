@@ -163,21 +163,28 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const int64_t pp_items = (int64_t)batch * heads_kv * (group % 2 ? group : group / 2) *
                            ((seqlen_q + pp_rows - 1) / pp_rows);
   // Causal tile pairs give the lower tile two fully masked key blocks per
-  // pair; measured against schedule 1 they win at 8192 rows (+3 %) and on a
-  // single round of pairs (MHA 4 x 16 x 1024: +10 %), lose at 1024-4096 rows
-  // over several rounds (-6 to -14 %); non-causal pairs win (+5 to +9 %).
+  // pair; measured against schedule 1 (head_dim 128) they win from 6144 rows
+  // (+5 to +13 % at 6144, +8 to +16 % at 8192-16384) and on a single round of
+  // pairs (MHA 4 x 16 x 1024: +10 %), and lose at 2048-4096 rows over several
+  // rounds (-2 to -3 %, +5 % for 1024 items); non-causal pairs win (+9 to +20 %).
   // Short tiles (below 2048 rows) over several rounds favour schedule 1 for
   // head pairs too (GQA 8 x 32/8 x 1024 causal: -5 %; 2048: +1.7 %; 4096:
   // +3.4 %): its two workgroups per CU overlap each other's tile starts.
   const bool one_round = pp_items <= L.num_cus;
-  const bool pairs_ok = group % 2 == 0 || !causal || seqlen_q >= 8192 || one_round;
+  const bool pairs_ok = group % 2 == 0 || !causal || seqlen_q >= 6144 || one_round;
   // A single causal round over at most kXcds (sequence, KV head) pairs: its
   // critical path is the heaviest item, which schedule 1 finishes 6-11 %
   // sooner (one sequence with 1, 4 or 8 KV heads, 1024-8192 rows, head pairs
   // and tile pairs alike); with 16 or more pairs the ping-pong wins (+9 to
   // +13 %).
   const bool few_pairs_round = causal && one_round && pairs <= fa::kXcds;
-  const bool pp_auto = pp_ok && pp_items >= L.num_cus && pairs_ok &&
+  // At head_dim 64 a key block carries half the matrix work of head_dim 128
+  // beside the same softmax, and the ping-pong measured slower than schedule 1
+  // on every shape tried (head pairs and tile pairs, causal or not, 1024-16384
+  // rows: -0.3 to -30 %, typically -4 to -10 %): it is taken for head_dim 128
+  // only.
+  const bool pp_dim = head_dim == 128;
+  const bool pp_auto = pp_ok && pp_dim && pp_items >= L.num_cus && pairs_ok &&
                        (seqlen_q >= 2048 || one_round) && !few_pairs_round;
   const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&

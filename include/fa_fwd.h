@@ -255,13 +255,13 @@ typedef struct fa_plan {
  *      epilogue).  It computes what schedule 3 computes; it measures slower
  *      on gfx950, where the hardware dispatcher already hands out schedule
  *      3's workgroups heaviest first as CUs free up.
- * The plan uses 4 where it applies, else 3 where it applies and its grid has
- * at least one workgroup per CU (`dev->num_cus`; smaller grids finish first
- * on schedule 1's finer tiles), from 2048 query rows unless its grid is a
- * single round (one workgroup per CU), with tile pairs under causal masking
- * only from 8192 query rows or for a single round, and not for a single
- * causal round over at most 8 (sequence, KV head) pairs; else 1, unless
- * fa_set_schedule forces one.
+ * The plan uses 4 where it applies, else 3 where it applies, head_dim is 128
+ * and its grid has at least one workgroup per CU (`dev->num_cus`; smaller
+ * grids finish first on schedule 1's finer tiles), from 2048 query rows
+ * unless its grid is a single round (one workgroup per CU), with tile pairs
+ * under causal masking only from 6144 query rows or for a single round, and
+ * not for a single causal round over at most 8 (sequence, KV head) pairs;
+ * else 1, unless fa_set_schedule forces one.
  */
 int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
                 int varlen, int head_dim, int head_dim_v, int causal,

@@ -226,8 +226,16 @@ def test_plan_gfx950():
     p12 = fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 3, 4, 4, 1024, 1024, False, 128, 128, True)
     assert (p12.schedule, p12.m_tiles, p12.num_workgroups) == (1, 8, 32 + 8 * 8)
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 2, 512, 512, False, 128, 128, True).schedule == 1
-    # causal tile pairs over several rounds below 8192 rows: schedule 1; non-causal: pairs
+    # causal tile pairs over several rounds below 6144 rows: schedule 1; non-causal: pairs
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 2048, 2048, False, 128, 128, True).schedule == 1
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 4096, 4096, False, 128, 128, True).schedule == 1
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 16, 16, 6144, 6144, False, 128, 128, True).schedule == 3
+    # head_dim 64: schedule 1 wherever the ping-pong would otherwise be taken
+    for args in ((2, 32, 8, 8192, True), (2, 32, 8, 8192, False), (2, 16, 16, 8192, True),
+                 (4, 16, 16, 4096, False), (2, 16, 16, 2048, False)):
+        b_, hq, hkv, s_, c = args
+        assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, b_, hq, hkv, s_, s_, False, 128, 128, c).schedule == 3
+        assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, b_, hq, hkv, s_, s_, False, 64, 64, c).schedule == 1
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 2048, 2048, False, 128, 128, False).schedule == 3
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 24, 8, 8192, 8192, False, 128, 128, True).schedule == 3
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 24, 8, 2048, 2048, False, 128, 128, True).schedule == 1
@@ -251,7 +259,8 @@ def test_plan_gfx950():
     # 8 heads x 4 rows = 32 columns still fits; 8 x 5 does not
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 4, 100, False, 64, 64, False).schedule == 4
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 1, 5, 100, False, 64, 64, False).schedule == 1
-    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 64, 8, 1, 5, 100, False, 64, 64, False).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 64, 8, 1, 5, 100, False, 128, 128, False).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 64, 8, 1, 5, 100, False, 64, 64, False).schedule == 1
     # a single causal round over at most 8 (sequence, kv-head) pairs: schedule 1; 16 pairs: 3
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 32, 8, 2048, 2048, False, 128, 128, True).schedule == 1
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 32, 1, 2048, 2048, False, 128, 128, True).schedule == 1
