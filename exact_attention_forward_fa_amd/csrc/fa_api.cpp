@@ -158,7 +158,12 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   // (and one workgroup on a CU): where that leaves CUs idle, schedule 1's
   // finer grid finishes first (the 2-head x 256-row case measured 8.6 us
   // against 6.2 us), so the automatic choice takes it only for grids of at
-  // least one workgroup per CU.
+  // least one workgroup per CU -- or, without causal masking, for more than
+  // half a round: there schedule 1's twice as many workgroups put two on
+  // some CUs, and the ping-pong measured +14 to +20 % (160-192 workgroups on
+  // 256 CUs, MHA and GQA, 1536-6144 rows; -14 to -16 % at exactly 128).
+  // Causal grids below a round stay on schedule 1 (0 to -19 % for the
+  // ping-pong).
   const int64_t pp_rows = group % 2 ? 2LL * fa::kTileM : fa::kTileM;
   const int64_t pp_items = (int64_t)batch * heads_kv * (group % 2 ? group : group / 2) *
                            ((seqlen_q + pp_rows - 1) / pp_rows);
@@ -184,7 +189,8 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   // rows: -0.3 to -30 %, typically -4 to -10 %): it is taken for head_dim 128
   // only.
   const bool pp_dim = head_dim == 128;
-  const bool pp_auto = pp_ok && pp_dim && pp_items >= L.num_cus && pairs_ok &&
+  const bool pp_fill = pp_items >= L.num_cus || (!causal && 2 * pp_items > L.num_cus);
+  const bool pp_auto = pp_ok && pp_dim && pp_fill && pairs_ok &&
                        (seqlen_q >= 2048 || one_round) && !few_pairs_round;
   const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&

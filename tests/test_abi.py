@@ -230,6 +230,12 @@ def test_plan_gfx950():
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 2048, 2048, False, 128, 128, True).schedule == 1
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 16, 16, 4096, 4096, False, 128, 128, True).schedule == 1
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 16, 16, 6144, 6144, False, 128, 128, True).schedule == 3
+    # grids below one workgroup per CU: non-causal ones of more than half a round take the
+    # ping-pong, causal ones schedule 1
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 16, 16, 3072, 3072, False, 128, 128, False).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 16, 4, 3072, 3072, False, 128, 128, False).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 8, 8, 4096, 4096, False, 128, 128, False).schedule == 1
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 1, 16, 16, 3072, 3072, False, 128, 128, True).schedule == 1
     # head_dim 64: schedule 1 wherever the ping-pong would otherwise be taken
     for args in ((2, 32, 8, 8192, True), (2, 32, 8, 8192, False), (2, 16, 16, 8192, True),
                  (4, 16, 16, 4096, False), (2, 16, 16, 2048, False)):
