@@ -172,9 +172,12 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   // (+5 to +13 % at 6144, +8 to +16 % at 8192-16384) and on a single round of
   // pairs (MHA 4 x 16 x 1024: +10 %), and lose at 2048-4096 rows over several
   // rounds (-2 to -3 %, +5 % for 1024 items); non-causal pairs win (+9 to +20 %).
-  // Short tiles (below 2048 rows) over several rounds favour schedule 1 for
-  // head pairs too (GQA 8 x 32/8 x 1024 causal: -5 %; 2048: +1.7 %; 4096:
-  // +3.4 %): its two workgroups per CU overlap each other's tile starts.
+  // Short causal sequences (below 2048 rows) over several rounds favour
+  // schedule 1 for head pairs too (GQA 32/8 causal at 512-1536 rows: -1 to
+  // -16 %; 2048: +1.7 %; 4096: +3.4 %): its two workgroups per CU overlap
+  // each other's tile starts.  Without causal masking the ping-pong wins from
+  // 1024 rows (+3 to +8 % on seven of nine MHA, GQA and group-3 shapes at
+  // 1024-1536 rows, -4 % on the other two; 512-768 rows: -4 to -7 %).
   const bool one_round = pp_items <= L.num_cus;
   const bool pairs_ok = group % 2 == 0 || !causal || seqlen_q >= 6144 || one_round;
   // A single causal round over at most kXcds (sequence, KV head) pairs: its
@@ -191,7 +194,7 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const bool pp_dim = head_dim == 128;
   const bool pp_fill = pp_items >= L.num_cus || (!causal && 2 * pp_items > L.num_cus);
   const bool pp_auto = pp_ok && pp_dim && pp_fill && pairs_ok &&
-                       (seqlen_q >= 2048 || one_round) && !few_pairs_round;
+                       (seqlen_q >= (causal ? 2048 : 1024) || one_round) && !few_pairs_round;
   const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&
                          L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;

@@ -258,7 +258,8 @@ typedef struct fa_plan {
  * The plan uses 4 where it applies, else 3 where it applies, head_dim is 128
  * and its grid has at least one workgroup per CU (`dev->num_cus`; smaller
  * grids finish first on schedule 1's finer tiles; without causal masking,
- * more than half a workgroup per CU suffices), from 2048 query rows
+ * more than half a workgroup per CU suffices), from 2048 query rows (1024
+ * without causal masking)
  * unless its grid is a single round (one workgroup per CU), with tile pairs
  * under causal masking only from 6144 query rows or for a single round, and
  * not for a single causal round over at most 8 (sequence, KV head) pairs;

@@ -247,6 +247,10 @@ def test_plan_gfx950():
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 24, 8, 2048, 2048, False, 128, 128, True).schedule == 1
     # head pairs below 2048 rows over several rounds: schedule 1; one round or 2048+: ping-pong
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 8, 32, 8, 1024, 1024, False, 128, 128, True).schedule == 1
+    # without causal masking from 1024 rows
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 8, 32, 8, 1024, 1024, False, 128, 128, False).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 8, 16, 16, 1024, 1024, False, 128, 128, False).schedule == 3
+    assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 32, 16, 16, 512, 512, False, 128, 128, False).schedule == 1
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 4, 32, 8, 2048, 2048, False, 128, 128, True).schedule == 3
     assert fa.fa_fwd_plan(fa.FA_DTYPE_BF16, 2, 32, 8, 1024, 1024, False, 128, 128, True).schedule == 3
     # packed varlen MHA stays on schedule 1 (128-row tiles, two workgroups per CU)
