@@ -273,10 +273,11 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
                  float softmax_scale, int causal, const float* descales, void* stream) {
   int rc = check_dims(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, head_dim_v);
   if (rc) return rc;
-  // Q/O/LSE may be NULL only when there is provably no query row, K/V only
-  // when there is provably no key (fixed-length calls with a zero length).
-  if ((!q || !o || !lse) && (cu_seqlens || seqlen_q > 0)) return FA_ERR_NULL;
-  if ((!k || !v) && (cu_seqlens || seqlen_k > 0)) return FA_ERR_NULL;
+  // Q/O/LSE may be NULL only when there is no query row, K/V only when there
+  // is no key: a zero length, for a packed batch a zero maximum (every
+  // sequence's length is at most the maximum passed).
+  if ((!q || !o || !lse) && seqlen_q > 0) return FA_ERR_NULL;
+  if ((!k || !v) && seqlen_k > 0) return FA_ERR_NULL;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
   const int dtype = descales ? FA_DTYPE_E4M3 : FA_DTYPE_BF16;

@@ -84,8 +84,9 @@ extern "C" {
  *               factors of e4m3 inputs: q*k descale multiplies the scores,
  *               v descale the output
  *
- * q, o and lse may be NULL only for a fixed-length call with seqlen_q == 0;
- * k and v only for a fixed-length call with seqlen_k == 0.
+ * q, o and lse may be NULL only when seqlen_q == 0, k and v only when
+ * seqlen_k == 0 (for a packed batch these are the maxima, so no sequence has
+ * a query row, or a key, to read).
  *
  * Returns FA_OK or a negative code (fa_strerror).  Rows of a sequence with
  * no admissible key get O = 0 and LSE = -inf; nothing is written for

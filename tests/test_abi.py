@@ -89,6 +89,21 @@ def test_validation_before_any_hip_call(kw, code):
 def test_empty_problem_is_a_no_op():
     # no query rows: nothing to launch, so no device is needed either
     assert call(q=None, o=None, lse=None, seqlen_q=0) == fa.FA_OK
+    # the same for a packed batch whose longest query length is 0
+    assert call(q=None, o=None, lse=None, seqlen_q=0, cu_seqlens=P) == fa.FA_OK
+
+
+@pytest.mark.parametrize("varlen", [False, True])
+def test_null_keys_only_without_keys(varlen):
+    """K and V may be NULL exactly when the (largest) key length is 0, Q/O/LSE when the
+    (largest) query length is 0: otherwise the call is refused before any HIP call.  (The
+    accepted form is checked here without query rows, so that nothing is launched on these
+    fake addresses; the GPU sweep runs a packed batch without keys on real buffers.)"""
+    cu = P if varlen else None
+    assert call(k=None, v=None, seqlen_k=1, cu_seqlens=cu) == fa.FA_ERR_NULL
+    assert call(q=None, seqlen_q=1, cu_seqlens=cu) == fa.FA_ERR_NULL
+    assert call(q=None, o=None, lse=None, k=None, v=None, seqlen_q=0, seqlen_k=0,
+                cu_seqlens=cu) == fa.FA_OK
 
 
 def _limits(name, fx):
