@@ -316,6 +316,9 @@ def main(argv=None) -> int:
     ap.add_argument("--exp2-offload", type=int, default=0, choices=[0, 4, 8],
                     help="ping-pong schedule: every N-th exponential on the FMA polynomial "
                          "(0: off, the default)")
+    ap.add_argument("--fp8-exact-scores", type=int, default=0, choices=[0, 1],
+                    help="e4m3 workloads: scores on the bf16 MFMA from exactly widened Q and K "
+                         "(1), or on the fp8 MFMA (0, the default)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES bytes (counter scaling) and exit")
     args = ap.parse_args(argv)
@@ -341,6 +344,7 @@ def main(argv=None) -> int:
         return run_kvcache(args, KVCACHE_WORKLOADS[args.workload])
     w = fa_inputs.workload(args.workload)
     fa.fa_set_exp2_offload(args.exp2_offload)
+    fa.fa_set_fp8_exact_scores(args.fp8_exact_scores)
     log(f"workload {w.name}: batch={w.batch} hq={w.heads_q} hkv={w.heads_kv} sq={w.seqlen_q} "
         f"sk={w.seqlen_k} d={w.head_dim} causal={w.causal} dtype={w.dtype}")
     # every input on the device first, then the per-configuration lines back to back (see
@@ -397,7 +401,8 @@ def main(argv=None) -> int:
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None if args.exp2_offload else load_traffic(w.name),
+                     "traffic": (None if args.exp2_offload or args.fp8_exact_scores
+                                 else load_traffic(w.name)),
                      "kernel_ms": round(kernel_ms, 5)},
         "cpu_baseline": cpu,
         "configs": configs,
@@ -408,6 +413,8 @@ def main(argv=None) -> int:
     }
     if args.exp2_offload:
         line["config"]["exp2_offload"] = args.exp2_offload
+    if args.fp8_exact_scores:
+        line["config"]["fp8_exact_scores"] = 1
     print(json.dumps(line), flush=True)
     return 0
 

@@ -8,7 +8,8 @@ through ctypes.  The names mirror the C ABI in ``include/fa_fwd.h``:
            cu_seqlens, head_dim, head_dim_v, softmax_scale, causal, descales,
            stream=None)
     fa_fwd_plan(...), fa_smem_screen(...), fa_gfx950_limits(), fa_strerror(code),
-    fa_set_schedule(n), fa_set_exp2_offload(every), fa_check_cu_seqlens(cu_host, ...)
+    fa_set_schedule(n), fa_set_exp2_offload(every), fa_set_fp8_exact_scores(on),
+    fa_check_cu_seqlens(cu_host, ...)
 
 ``forward(q, k, v, ...)`` is a convenience that allocates O and LSE with torch
 and calls ``fa_fwd``.  There is no fallback: if the library is missing the
@@ -33,6 +34,7 @@ from ._binding import (  # noqa: F401
     fa_fwd_plan,
     fa_set_schedule,
     fa_set_exp2_offload,
+    fa_set_fp8_exact_scores,
     fa_gfx950_limits,
     fa_smem_screen,
     fa_strerror,

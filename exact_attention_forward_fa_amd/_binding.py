@@ -86,6 +86,8 @@ def _load():
     lib.fa_set_schedule.restype = i32
     lib.fa_set_exp2_offload.argtypes = [i32]
     lib.fa_set_exp2_offload.restype = i32
+    lib.fa_set_fp8_exact_scores.argtypes = [i32]
+    lib.fa_set_fp8_exact_scores.restype = i32
     lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                    i32, i32, ctypes.c_float, i32, vp, vp]
     lib.fa_fwd_kvcache.restype = i32
@@ -121,6 +123,14 @@ def fa_set_exp2_offload(every: int) -> None:
     rc = _lib.fa_set_exp2_offload(int(every))
     if rc != 0:
         raise FaError(rc, "fa_set_exp2_offload")
+
+
+def fa_set_fp8_exact_scores(on: int) -> None:
+    """e4m3 inputs: 1 computes the scores on the bf16 matrix instruction from exactly widened Q
+    and K (no loss of precision in the product), 0 (default) on the fp8 one."""
+    rc = _lib.fa_set_fp8_exact_scores(int(on))
+    if rc != 0:
+        raise FaError(rc, "fa_set_fp8_exact_scores")
 
 
 def fa_gfx950_limits() -> DeviceLimits:

@@ -20,6 +20,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 std::atomic<int> g_schedule{0};
 // fa_set_exp2_offload: 0, 4 or 8
 std::atomic<int> g_exp2_offload{0};
+// fa_set_fp8_exact_scores: 0 or 1
+std::atomic<int> g_fp8_exact{0};
 
 // gfx950 (MI355X): 160 KiB LDS per CU, all of it addressable by one
 // workgroup; 256 CUs; 4 SIMDs per CU; 512 VGPR+AGPR per lane per SIMD;
@@ -75,6 +77,12 @@ int fa_set_schedule(int schedule) {
 int fa_set_exp2_offload(int every) {
   if (every != 0 && every != 4 && every != 8) return FA_ERR_INVALID;
   g_exp2_offload.store(every, std::memory_order_relaxed);
+  return FA_OK;
+}
+
+int fa_set_fp8_exact_scores(int on) {
+  if (on != 0 && on != 1) return FA_ERR_INVALID;
+  g_fp8_exact.store(on, std::memory_order_relaxed);
   return FA_OK;
 }
 
@@ -336,6 +344,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
                           : plan.num_workgroups;
   L.decode = plan.schedule == 4;
   L.exp2_offload = L.pingpong ? g_exp2_offload.load(std::memory_order_relaxed) : 0;
+  L.fp8_exact = L.fp8 ? g_fp8_exact.load(std::memory_order_relaxed) : 0;
   return fa::launch(L, stream);
 }
 

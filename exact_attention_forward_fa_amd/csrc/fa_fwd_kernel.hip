@@ -1425,6 +1425,13 @@ void fa_fwd_bf16_decode_kernel(Params p) {
 //  * The q and k descales fold into the exp2 scale (the forward-pass page's
 //    FP8 branch multiplies softmax_scale_log2 by q_descale * k_descale); the
 //    v descale multiplies O in the epilogue.
+//  * XS (exact scores, opt-in): S^T = K Q^T on the bf16 MFMA instead, with
+//    Q and K widened from e4m3 to bf16 (exactly: every e4m3 value is a bf16
+//    value).  The fp8 matrix instruction keeps only about 13-14 bits below
+//    the largest product of each dot product, so a row whose scores are far
+//    above its other products loses precision in its LSE; the bf16 product is
+//    exact.  K is widened per operand read (8 bytes -> 8 bf16, four
+//    conversions), Q once per tile.  P V stays on the fp8 MFMA.
 
 // LDS row of a K block (fp8) -> key: row 32t + rho holds key
 // 32((rho>>2)&1) + 16t + 4(rho>>3) + (rho&3), i.e. the key of accumulator
@@ -1457,7 +1464,17 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 // is the column sum of P^T in every row.
 constexpr int kE4m3OnesWord = 0x38383838;
 
-template <int D, bool CAUSAL>
+// Eight e4m3 bytes -> eight bf16 values (exact).
+__device__ __forceinline__ bf16x8 widen_e4m3(const u32x2 w) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int D, bool CAUSAL, bool XS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_fp8_kernel(Params p) {
   constexpr int TM = kTileM, TN = kTileN;
@@ -1466,6 +1483,7 @@ void fa_fwd_fp8_kernel(Params p) {
   constexpr int CPR = D / 16;                // 16-byte chunks per row
   constexpr int NI = TN * CPR / 256;         // direct-load instructions per wave per block
   constexpr int KC = D / 64;                 // 64-wide k-chunks of the QK^T product
+  constexpr int KC16 = D / 16;               // 16-wide k-chunks of the bf16 product (XS)
   constexpr int DT = D / 32;                 // 32-wide output tiles of O^T
   __shared__ __attribute__((aligned(1024))) char smem[4 * BUF];
   char* const kbuf0 = smem;
@@ -1512,15 +1530,26 @@ void fa_fwd_fp8_kernel(Params p) {
     return;
   }
 
-  // ---- Q fragments: lane holds Q[qi][64kc + 32hf .. +31]
-  i32x8 qf[KC];
+  // ---- Q fragments: lane holds Q[qi][64kc + 32hf .. +31]; XS: the e4m3
+  // bytes Q[qi][16kc + 8hf .. +7] of the bf16 B operand of k-chunk kc,
+  // widened where they are used (kept narrow: 16 registers instead of 32)
+  i32x8 qf[XS ? 1 : KC];
+  u32x2 qh[XS ? KC16 : 1];
+  if constexpr (!XS) {
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    const unsigned char* qp = Q + qrow + 64 * kc + 32 * hf;
-    u32x4 lo = qvalid ? *(const u32x4*)qp : u32x4{0u, 0u, 0u, 0u};
-    u32x4 hi = qvalid ? *(const u32x4*)(qp + 16) : u32x4{0u, 0u, 0u, 0u};
-    qf[kc] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    for (int kc = 0; kc < KC; ++kc) {
+      const unsigned char* qp = Q + qrow + 64 * kc + 32 * hf;
+      u32x4 lo = qvalid ? *(const u32x4*)qp : u32x4{0u, 0u, 0u, 0u};
+      u32x4 hi = qvalid ? *(const u32x4*)(qp + 16) : u32x4{0u, 0u, 0u, 0u};
+      qf[kc] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < KC16; ++kc) {
+      const unsigned char* qp = Q + qrow + 16 * kc + 8 * hf;
+      qh[kc] = qvalid ? *(const u32x2*)qp : u32x2{0u, 0u};
+    }
   }
 
   // ---- direct buffer -> LDS staging
@@ -1558,20 +1587,35 @@ void fa_fwd_fp8_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) ka[kc][j] = r32 * RB + (((4 * kc + 2 * hf + j) ^ x) * 16);
   }
+  // XS: the bf16 A operand of k-chunk kc is row 32t + r32, bytes 16kc + 8hf
+  // .. +7, in logical 16-byte column kc
+  auto k16_operand = [&](const char* kb, int t, int kc) __attribute__((always_inline)) {
+    const int x = swz_k8<D>(r32);
+    return widen_e4m3(*(const u32x2*)(kb + 32 * t * RB + r32 * RB + ((kc ^ x) * 16) + 8 * hf));
+  };
   auto k_operand = [&](const char* kb, int t, int kc) __attribute__((always_inline)) {
     u32x4 lo = *(const u32x4*)(kb + 32 * t * RB + ka[kc][0]);
     u32x4 hi = *(const u32x4*)(kb + 32 * t * RB + ka[kc][1]);
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
+  // one of the score MFMAs: fp8 (step i of 2 * KC: k-chunk i >> 1, sub-tile
+  // i & 1) or, XS, bf16 (step i of 2 * KC16)
+  auto score_mfma = [&](const char* kb, f32x16* s, const int i) __attribute__((always_inline)) {
+    const int kc = i >> 1, t = i & 1;
+    if constexpr (!XS)
+      s[t] = mfma_fp8(k_operand(kb, t, kc), qf[kc], s[t]);
+    else
+      s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k16_operand(kb, t, kc), widen_e4m3(qh[kc]),
+                                                     s[t], 0, 0, 0);
+  };
+  constexpr int NSC = XS ? 2 * KC16 : 2 * KC;  // score MFMAs per block
   auto qk = [&](int buf, f32x16* s) __attribute__((always_inline)) {
     const char* kb = kbuf0 + buf * BUF;
 #pragma unroll
     for (int t = 0; t < 2; ++t) s[t] = f32x16{};
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) s[t] = mfma_fp8(k_operand(kb, t, kc), qf[kc], s[t]);
+    for (int i = 0; i < NSC; ++i) score_mfma(kb, s, i);
   };
 
   // V^T operand of dv tile dt: lane = 16G + 2t' + u reads 8 bytes of key row
@@ -1658,31 +1702,36 @@ void fa_fwd_fp8_kernel(Params p) {
       word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
       pb[w] = word;
     };
+    if constexpr (!XS) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) sn[t] = f32x16{};
+      for (int t = 0; t < 2; ++t) sn[t] = f32x16{};
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      if ((w & 1) == 0 && (w >> 1) < 2 * KC) {
-        const int i = w >> 1, kc = i >> 1, t = i & 1;
-        sn[t] = mfma_fp8(k_operand(kread, t, kc), qf[kc], sn[t]);
+      for (int w = 0; w < 8; ++w) {
+        if ((w & 1) == 0 && (w >> 1) < NSC) score_mfma(kread, sn, w >> 1);
+        pword(m_run * c, w);
       }
-      pword(m_run * c, w);
-    }
-    // each of the four score MFMAs followed by a quarter of the softmax (8
-    // exponentials, 16 other vector instructions); left to itself the
-    // compiler groups the MFMAs after the softmax (measured 1.2 % slower)
+      // each of the four score MFMAs followed by a quarter of the softmax (8
+      // exponentials, 16 other vector instructions); left to itself the
+      // compiler groups the MFMAs after the softmax (measured 1.2 % slower)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sched_group(kSchedMfma, 1);
-      sched_group(kSchedTrans, 8);
-      sched_group(kSchedValu, 16);
+      for (int i = 0; i < 4; ++i) {
+        sched_group(kSchedMfma, 1);
+        sched_group(kSchedTrans, 8);
+        sched_group(kSchedValu, 16);
+      }
+    } else {
+      // the next block's scores after this block's P V (below): its tiles
+      // then never live beside this block's, which keeps the kernel in 256
+      // registers
+#pragma unroll
+      for (int w = 0; w < 8; ++w) pword(m_run * c, w);
     }
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= kLazyBound)) != 0, 0)) {
       // The next block's scores are read on this (rare) path so that their
       // MFMAs stay where the schedule hints put them, among the exponentials:
       // otherwise the compiler sinks them past the branch, after the softmax
       // (non-causal +1.9 %; the causal kernel then runs out of registers)
-      if constexpr (!CAUSAL) asm volatile("" ::"v"(sn[0]), "v"(sn[1]));
+      if constexpr (!CAUSAL && !XS) asm volatile("" ::"v"(sn[0]), "v"(sn[1]));
       const float m_new = fmax_nan(m_run, halfwave_max(block_max(sc)));
       if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
         const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
@@ -1712,6 +1761,12 @@ void fa_fwd_fp8_kernel(Params p) {
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[t] = mfma_fp8(va_op[t], pb, oacc[t]);
     lq = mfma_fp8(ones, pb, lq);
+    if constexpr (XS) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sn[t] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < NSC; ++i) score_mfma(kread, sn, i);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
   char* const k0b = kbuf0;
@@ -1752,8 +1807,12 @@ void fa_fwd_fp8_kernel(Params p) {
 
 template <int D, bool CAUSAL>
 void launch_fp8(const Launch& L, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)L.num_workgroups), dim3(256),
-                     0, stream, L.p);
+  if (L.fp8_exact)
+    hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL, true>), dim3((unsigned)L.num_workgroups),
+                       dim3(256), 0, stream, L.p);
+  else
+    hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL, false>), dim3((unsigned)L.num_workgroups),
+                       dim3(256), 0, stream, L.p);
 }
 
 template <int D, bool CAUSAL>

@@ -68,6 +68,7 @@ struct Launch {
   int decode;       // 1: the decode kernel (bf16, a KV head's query rows in one tile)
   int exp2_offload; // ping-pong only: 0, or every 4th / 8th exponential on the FMA polynomial
   int persist;      // ping-pong only: 1 for the persistent kernel (num_items items)
+  int fp8_exact;    // fp8 only: 1 for scores on the bf16 MFMA from widened Q and K
   int64_t num_items;
   int64_t num_workgroups;
 };

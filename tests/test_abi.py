@@ -364,6 +364,18 @@ def test_exp2_offload_setting():
         fa.fa_set_exp2_offload(0)
 
 
+def test_fp8_exact_scores_setting():
+    try:
+        for ok in (1, 0):
+            fa.fa_set_fp8_exact_scores(ok)
+        for bad in (-1, 2, 8):
+            with pytest.raises(fa.FaError) as e:
+                fa.fa_set_fp8_exact_scores(bad)
+            assert e.value.code == fa.FA_ERR_INVALID
+    finally:
+        fa.fa_set_fp8_exact_scores(0)
+
+
 def test_plan_reports_unsupported_when_nothing_fits():
     small = fa.DeviceLimits(lds_bytes_per_block=48 * KIB, lds_bytes_per_cu=48 * KIB, num_cus=1,
                             simds_per_cu=4, regs_per_simd_lane=512, max_waves_per_simd=8)

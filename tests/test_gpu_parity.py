@@ -299,7 +299,8 @@ def test_running_max_growth(shape, causal, pattern, schedule):
 # scores, carries an error of about 1e-4 of them: inside the fp8 LSE tolerance (5e-3) up to
 # scores of about 50.  The causal steep ramp reaches 58.7.
 FP8_SCORE_PRECISION = ("fp8 MFMA accumulation keeps ~14 bits relative to the scores: LSE error "
-                       "5.9e-3 at |LSE| = 58.7 (causal ramp10, 520 keys), above 5e-3")
+                       "5.9e-3 at |LSE| = 58.7 (causal ramp10, 520 keys), above 5e-3; "
+                       "fa_set_fp8_exact_scores(1) meets it (test_fp8_exact_scores_*)")
 
 
 @pytest.mark.parametrize("pattern", GROWTH_PATTERNS)
@@ -394,6 +395,58 @@ def test_fp8_varlen():
     w = fa_inputs.make(0, 4, 2, 0, 0, 128, causal=True, seed=70, lengths=lens, dtype="e4m3",
                        name="fp8_varlen_small")
     full_check(w)
+
+
+# ---------------------------------------- fp8 with exact scores (opt-in switch)
+
+
+@pytest.fixture
+def fp8_exact():
+    """fa_set_fp8_exact_scores(1) for the test: Q K^T on the bf16 matrix instruction from Q and
+    K widened exactly from e4m3."""
+    import exact_attention_forward_fa_amd as fa
+
+    fa.fa_set_fp8_exact_scores(1)
+    yield
+    fa.fa_set_fp8_exact_scores(0)
+
+
+@pytest.mark.parametrize("pattern", GROWTH_PATTERNS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_exact_scores_running_max_growth(causal, pattern, fp8_exact):
+    """The growth patterns of test_fp8_running_max_growth with exact scores: all within the
+    fp8 tolerance, the causal steep ramp (|LSE| = 58.7) included."""
+    s = 520
+    w = fa_inputs.make(1, 4, 2, s, s, 128, causal=causal, seed=90 + GROWTH_PATTERNS.index(pattern),
+                       dtype="e4m3", key_offsets=key_offset_pattern(pattern, s),
+                       name=f"fp8x_growth_{pattern}_s{s}_c{int(causal)}")
+    full_check(w)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 4, 4, 300, 300), (1, 8, 2, 200, 517), (1, 4, 1, 517, 200),
+                                   (1, 2, 2, 1, 1)])
+def test_fp8_exact_scores_ragged_shapes(shape, causal, d, fp8_exact):
+    b, hq, hkv, sq, sk = shape
+    w = fa_inputs.make(b, hq, hkv, sq, sk, d, causal=causal, seed=sq * 5 + sk + d + 1, dtype="e4m3",
+                       name=f"fp8x_b{b}_hq{hq}_hkv{hkv}_sq{sq}_sk{sk}_d{d}_c{int(causal)}")
+    full_check(w)
+
+
+def test_fp8_exact_scores_large_q_and_varlen(fp8_exact):
+    full_check(fa_inputs.make(1, 4, 2, 256, 256, 128, causal=True, seed=61, q_mult=50.0,
+                              dtype="e4m3", name="fp8x_q_x50"))
+    full_check(fa_inputs.make(1, 4, 2, 512, 512, 128, causal=True, seed=62, q_mult=20.0,
+                              dtype="e4m3", name="fp8x_q_x20"))
+    lens = [(300, 517), (1, 64), (129, 100), (64, 0), (0, 40), (255, 256)]
+    full_check(fa_inputs.make(0, 4, 2, 0, 0, 128, causal=True, seed=70, lengths=lens,
+                              dtype="e4m3", name="fp8x_varlen_small"))
+
+
+def test_fp8_exact_scores_16384_sampled(fp8_exact):
+    """The fp8 workload with exact scores, every tile sampled against the oracle."""
+    sampled_check(fa_inputs.workload("fp8_causal_b1_h32_s16384_d128"))
 
 
 # ------------------------------------------------------- KV cache (AppendKV)
