@@ -555,6 +555,13 @@ def test_kvcache_fp8():
     kvcache_check(case, "kv_fp8")
 
 
+def test_kvcache_fp8_exact_scores(fp8_exact):
+    """The KV-cache entry point takes the fp8 exact-score switch as fa_fwd does."""
+    case = fa_inputs.make_kvcache(2, 130, 70, 1024, [0, 400], 4, 2, 128, causal=True, seed=86,
+                                  dtype="e4m3")
+    kvcache_check(case, "kv_fp8_exact")
+
+
 # ------------------------------------------------------------ graph capture
 
 @pytest.mark.parametrize("case", ["gqa_pingpong", "mha_pairs", "varlen", "fp8", "decode"])
