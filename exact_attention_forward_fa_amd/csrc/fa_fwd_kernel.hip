@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/fa_fwd.h"
 #include "fa_exp2_poly.h"
 #include "fa_internal.h"
@@ -1873,17 +1875,21 @@ __global__ __launch_bounds__(256) void append_kv_kernel(Append a) {
 }
 
 int device_is_gfx950() {
-  static int cached[64];  // 0 unknown, 1 yes, -1 no
+  // per device: 0 unknown, 1 yes, -1 no (atomic: host threads may launch
+  // concurrently; a first query made twice stores the same answer)
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
     const char* a = prop.gcnArchName;
-    cached[dev] = (a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
-                   a[5] == '0') ? 1 : -1;
+    v = (a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' && a[5] == '0')
+            ? 1 : -1;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev] == 1;
+  return v == 1;
 }
 
 }  // namespace
