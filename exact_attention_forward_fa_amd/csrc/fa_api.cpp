@@ -203,7 +203,8 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const bool pp_fill = pp_items >= L.num_cus || (!causal && 2 * pp_items > L.num_cus);
   const bool pp_auto = pp_ok && pp_dim && pp_fill && pairs_ok &&
                        (seqlen_q >= (causal ? 2048 : 1024) || one_round) && !few_pairs_round;
-  const int64_t decode_lds = 4LL * fa::kDecodeSlots * 2 * 32 * head_dim * 2;  // 4 waves, K + V
+  // each wave's ring of K and V slots of 32 keys
+  const int64_t decode_lds = (int64_t)fa::kDecodeWaves * fa::kDecodeSlots * 2 * 32 * head_dim * 2;
   const bool decode_ok = bf16 && (int64_t)group * seqlen_q <= 32 && seqlen_q > 0 &&
                          L.regs_per_simd_lane >= 512 && decode_lds <= L.lds_bytes_per_block;
   const int forced = g_schedule.load(std::memory_order_relaxed);
@@ -218,7 +219,7 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   if (sched == 4) {
     out->tile_m = 32;  // (query head, row) columns of one tile
     out->tile_n = 32;
-    out->waves = 4;
+    out->waves = fa::kDecodeWaves;
     out->kv_stages = fa::kDecodeSlots;
     out->lds_bytes = decode_lds;
     out->wg_per_cu = 1;

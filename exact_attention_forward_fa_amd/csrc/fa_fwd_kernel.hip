@@ -1177,7 +1177,7 @@ void fa_fwd_bf16_decode_kernel(Params p) {
   constexpr int KC = D / 16;             // k-chunks of QK^T
   constexpr int DT = D / 32;             // 32-dim tiles of O^T
   constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int NWV = 4;                 // waves
+  constexpr int NWV = kDecodeWaves;      // waves
   constexpr int VI = TK * CPR / 64;      // direct-load instructions per V block
   constexpr int BLK_LOADS = 2 * VI;      // memory instructions per block and wave
   static_assert(DEPTH * BLK_LOADS <= 63, "vmcnt counts up to 63");
@@ -1837,7 +1837,7 @@ template <int D, bool CAUSAL>
 void launch_bf16(const Launch& L, hipStream_t stream) {
   if (L.decode) {
     hipLaunchKernelGGL((fa_fwd_bf16_decode_kernel<D, CAUSAL>), dim3((unsigned)L.num_workgroups),
-                       dim3(256), 0, stream, L.p);
+                       dim3(64 * kDecodeWaves), 0, stream, L.p);
     return;
   }
   if (L.pingpong) {

@@ -15,7 +15,11 @@ constexpr int kXcds = 8;     // XCDs of an MI355X; workgroups go round-robin ove
 #ifndef DEC_SLOTS
 #define DEC_SLOTS 2
 #endif
+#ifndef DEC_WAVES
+#define DEC_WAVES 4
+#endif
 constexpr int kDecodeSlots = DEC_SLOTS;  // K and V LDS ring slots per wave of the decode kernel
+constexpr int kDecodeWaves = DEC_WAVES;  // waves of the decode kernel (they split the keys)
 
 // LDS per workgroup: K and V blocks of kTileN rows of d*2 bytes (no padding;
 // bank conflicts are avoided by swizzling 16-byte columns), double-buffered.
