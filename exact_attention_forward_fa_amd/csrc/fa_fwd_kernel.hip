@@ -8,9 +8,11 @@
 //     with an odd number of query heads per KV head, two adjacent query tiles of one), the
 //     two groups of waves alternating GEMM and softmax phases (ping-pong);
 //  4. fa_fwd_bf16_decode_kernel: a KV head's (query head, row) pairs in one
-//     32-column tile, the 4 waves splitting the key range;
+//     32-column tile, the waves (DEC_WAVES, 4) splitting the key range;
 //  5. fa_fwd_bf16_pp_persist_kernel (forced only): schedule 3's items walked
 //     by resident workgroups that prefetch their next item's query rows.
+// fa_fwd_fp8_kernel<.., XS = true> is the e4m3 kernel with its scores on the
+// bf16 matrix instruction from exactly widened Q and K (opt-in).
 // The description below is that of schedule 1; the others say how they
 // differ.  One workgroup = 4 wavefronts = 128 query rows of one (sequence,
 // head).  Each wave owns 32 query rows and walks the key blocks (64 keys
