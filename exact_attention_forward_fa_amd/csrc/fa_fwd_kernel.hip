@@ -1180,6 +1180,8 @@ void fa_fwd_bf16_decode_kernel(Params p) {
   constexpr int DT = D / 32;             // 32-dim tiles of O^T
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int NWV = kDecodeWaves;      // waves
+  static_assert(NWV >= 1 && NWV <= 4,
+                "one wave per SIMD: the kernel holds the full 512-register file");
   constexpr int VI = TK * CPR / 64;      // direct-load instructions per V block
   constexpr int BLK_LOADS = 2 * VI;      // memory instructions per block and wave
   static_assert(DEPTH * BLK_LOADS <= 63, "vmcnt counts up to 63");
