@@ -16,7 +16,7 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// fa_set_schedule: 0 automatic, else the forced schedule (1 .. 4)
+// fa_set_schedule: 0 automatic, else the forced schedule (1 .. 5)
 std::atomic<int> g_schedule{0};
 // fa_set_exp2_offload: 0, 4 or 8
 std::atomic<int> g_exp2_offload{0};
@@ -115,8 +115,6 @@ int fa_smem_screen(const fa_tile_config_t* cfg, const fa_device_limits_t* dev, f
 int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
                 int varlen, int head_dim, int head_dim_v, int causal,
                 const fa_device_limits_t* dev, fa_plan_t* out) {
-  (void)varlen;
-  (void)causal;
   if (!out) return FA_ERR_NULL;
   int rc = check_dims(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, head_dim_v);
   if (rc) return rc;
@@ -240,7 +238,6 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   const bool mpair = pp && group % 2 == 1;
   const int heads_per_wg = pp && !mpair ? 2 : 1;
   const int vgprs = 256 * qt;
-  const int by_lds = (int)(L.lds_bytes_per_cu / lds);
   const int by_regs = (L.regs_per_simd_lane / vgprs) * L.simds_per_cu / waves;
   out->tile_m = fa::kTileM * (mpair ? 2 : qt);
   out->tile_n = fa::kTileN;
@@ -249,7 +246,6 @@ int fa_fwd_plan(int dtype, int batch, int heads_q, int heads_kv, int seqlen_q, i
   out->lds_bytes = sched == 5 ? lds + q_stage : lds;
   const int by_lds_s = (int)(L.lds_bytes_per_cu / out->lds_bytes);
   out->wg_per_cu = by_lds_s < by_regs ? by_lds_s : by_regs;
-  (void)by_lds;
   out->vgprs_per_lane = vgprs;
   out->query_tiles = qt;
   out->heads_per_workgroup = heads_per_wg;
